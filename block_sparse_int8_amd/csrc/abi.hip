@@ -1,0 +1,274 @@
+// C ABI of libsparse_attn: argument validation, device check, dispatch.
+//
+// Every entry point validates all of its arguments before queueing anything,
+// returns a status code, and records a message in a thread-local buffer
+// (FlashVSR Kitchen Sparse Attention, "When it bites": fail at once with a
+// clear message; unsupported runtimes are rejected outright).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/sparse_attn.h"
+#include "sa_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t ok() {
+  g_err[0] = '\0';
+  return SA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDev = 64;
+int g_arch[kMaxDev] = {0};
+std::mutex g_arch_mu;
+
+int32_t check_device(int dev) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(SA_E_DEVICE, "no HIP device is visible");
+  }
+  if (dev < 0 || dev >= count || dev >= kMaxDev) return fail(SA_E_DEVICE, "device %d does not exist (%d visible)", dev, count);
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_arch[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(SA_E_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    }
+    g_arch[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (g_arch[dev] == 2)
+      return fail(SA_E_UNSUPPORTED, "device %d is %s; this library only runs on gfx950 (MI355X)", dev,
+                  prop.gcnArchName);
+  }
+  if (g_arch[dev] != 1) return fail(SA_E_UNSUPPORTED, "device %d is not gfx950", dev);
+  return SA_OK;
+}
+
+int32_t check_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SA_E_DEVICE, "no current HIP device");
+  }
+  return check_device(dev);
+}
+
+int32_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SA_E_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool pos(int x) { return x > 0; }
+
+// Shared validation of dims / params for route and fwd.
+int32_t check_dims(const sa_dims* dm, const sa_route_params* p, bool has_vbs) {
+  if (!dm || !p) return fail(SA_E_NULL, "dims and params must not be NULL");
+  if (!pos(dm->B) || !pos(dm->H)) return fail(SA_E_SHAPE, "B and H must be >= 1 (got %d, %d)", dm->B, dm->H);
+  if (dm->d != 64 && dm->d != 128) return fail(SA_E_SHAPE, "d must be 64 or 128 (got %d)", dm->d);
+  if (dm->Lq < 0 || dm->Lq % 128) return fail(SA_E_SHAPE, "Lq must be a non-negative multiple of 128 (got %d)", dm->Lq);
+  if (dm->Lkv < 0 || dm->Lkv % 128) return fail(SA_E_SHAPE, "Lkv must be a non-negative multiple of 128 (got %d)", dm->Lkv);
+  if (dm->lq_valid < 0 || dm->lq_valid > dm->Lq) return fail(SA_E_SHAPE, "lq_valid %d outside [0, %d]", dm->lq_valid, dm->Lq);
+  if (dm->lkv_valid < 0 || dm->lkv_valid > dm->Lkv)
+    return fail(SA_E_SHAPE, "lkv_valid %d outside [0, %d]", dm->lkv_valid, dm->Lkv);
+  if (p->kblock != 64 && p->kblock != 128) return fail(SA_E_VALUE, "kblock must be 64 or 128 (got %d)", p->kblock);
+  if (p->k_scale_rows != 64 && p->k_scale_rows != 128)
+    return fail(SA_E_VALUE, "k_scale_rows must be 64 or 128 (got %d)", p->k_scale_rows);
+  if (p->centroids_per_block < 0 || p->centroids_per_block > 2)
+    return fail(SA_E_VALUE, "centroids_per_block must be 0, 1 or 2 (got %d)", p->centroids_per_block);
+  if (p->prefix_tokens < 0 || p->prefix_tokens % p->kblock)
+    return fail(SA_E_VALUE, "prefix_tokens must be a non-negative multiple of kblock (got %d)", p->prefix_tokens);
+  if (has_vbs) {
+    if (dm->Lv <= 0 || dm->Lv % 64) return fail(SA_E_SHAPE, "Lv must be a positive multiple of 64 with v_block_src (got %d)", dm->Lv);
+  } else if (dm->Lv != dm->Lkv) {
+    return fail(SA_E_SHAPE, "Lv (%d) must equal Lkv (%d) without v_block_src", dm->Lv, dm->Lkv);
+  }
+  if (dm->Lkv / p->kblock > 65535 * 2) return fail(SA_E_SHAPE, "Lkv too long");
+  return SA_OK;
+}
+
+int32_t check_v(int32_t v_dtype, const void* v, const float* v_scale, const sa_dims* dm, const sa_route_params* p) {
+  if (v_dtype != SA_BF16 && v_dtype != SA_INT8) return fail(SA_E_VALUE, "v_dtype must be SA_BF16 or SA_INT8");
+  if (!v) return fail(SA_E_NULL, "v must not be NULL");
+  if (!aligned16(v)) return fail(SA_E_ALIGN, "v must be 16-byte aligned");
+  if (v_dtype == SA_INT8) {
+    if (!v_scale) return fail(SA_E_NULL, "v_scale is required for INT8 V");
+    if (p->v_scale_rows != 64 && p->v_scale_rows != 128)
+      return fail(SA_E_VALUE, "v_scale_rows must be 64 or 128 (got %d)", p->v_scale_rows);
+    if (dm->Lv % p->v_scale_rows) return fail(SA_E_SHAPE, "Lv must be a multiple of v_scale_rows");
+  }
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sa_abi_version(void) { return SA_ABI_VERSION; }
+
+const char* sa_last_error(void) { return g_err; }
+
+int32_t sa_device_check(int32_t device) {
+  const int32_t rc = check_device(device);
+  return rc == SA_OK ? ok() : rc;
+}
+
+int32_t quantize_qk_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL, int32_t B, int32_t H,
+                         int32_t L, int32_t d, int32_t valid_len, int32_t rows_per_block, int8_t* x_q,
+                         float* scale, void* stream) {
+  if (!x_bf16 || !x_q || !scale) return fail(SA_E_NULL, "quantize_qk_int8: x, x_q and scale must not be NULL");
+  if (B < 1 || H < 1 || L < 0) return fail(SA_E_SHAPE, "quantize_qk_int8: bad B/H/L (%d, %d, %d)", B, H, L);
+  if (d != 64 && d != 128) return fail(SA_E_SHAPE, "quantize_qk_int8: d must be 64 or 128 (got %d)", d);
+  if (rows_per_block != 64 && rows_per_block != 128)
+    return fail(SA_E_VALUE, "quantize_qk_int8: rows_per_block must be 64 or 128 (got %d)", rows_per_block);
+  if (L % rows_per_block) return fail(SA_E_SHAPE, "quantize_qk_int8: L (%d) must be a multiple of rows_per_block", L);
+  if (valid_len < 0 || valid_len > L) return fail(SA_E_SHAPE, "quantize_qk_int8: valid_len %d outside [0, %d]", valid_len, L);
+  if (!aligned16(x_bf16) || !aligned16(x_q)) return fail(SA_E_ALIGN, "quantize_qk_int8: x and x_q must be 16-byte aligned");
+  if (sB % 8 || sH % 8 || sL % 8 || sL < d)
+    return fail(SA_E_ALIGN, "quantize_qk_int8: strides must be multiples of 8 elements and sL >= d");
+  if (const int32_t rc = check_current_device()) return rc;
+  if (L == 0) return ok();
+  sa::QuantizeArgs a{static_cast<const uint16_t*>(x_bf16), sB, sH, sL, B, H, L, d, valid_len, rows_per_block, x_q, scale};
+  return launched(sa::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize");
+}
+
+size_t sparse_attn_route_workspace_size(const sa_dims* dims, const sa_route_params* p, int32_t has_explicit_map) {
+  if (check_dims(dims, p, false) != SA_OK && check_dims(dims, p, true) != SA_OK) return 0;
+  if (has_explicit_map) return 0;
+  return sa::route_workspace_bytes(dims->B, dims->H, dims->Lq / 128, dims->Lkv / p->kblock, dims->d);
+}
+
+int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale, const void* v, int32_t v_dtype,
+                          const float* v_scale, const int32_t* v_block_src, const sa_dims* dims,
+                          const sa_route_params* p, const uint8_t* explicit_map, uint8_t* block_map,
+                          float* k_centroid, float* v_centroid, float* count, double* row_stats, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (const int32_t rc = check_dims(dims, p, v_block_src != nullptr)) return rc;
+  if (!q || !k || !k_scale || !block_map) return fail(SA_E_NULL, "sparse_attn_route: q, k, k_scale and block_map are required");
+  if (!aligned16(q) || !aligned16(k)) return fail(SA_E_ALIGN, "sparse_attn_route: q and k must be 16-byte aligned");
+  const int G = p->centroids_per_block;
+  const bool sol = explicit_map == nullptr;
+  if (sol) {
+    if (G == 0) return fail(SA_E_VALUE, "sparse_attn_route: the Sol rule needs centroids_per_block 1 or 2");
+    if (isnan(p->threshold)) return fail(SA_E_VALUE, "sparse_attn_route: threshold is NaN");
+    if (p->k_scale_rows != p->kblock)
+      return fail(SA_E_VALUE, "sparse_attn_route: the Sol rule needs one K scale per key block (k_scale_rows == kblock)");
+    if ((size_t)(dims->Lkv / p->kblock) * 8 > 49152)
+      return fail(SA_E_SHAPE, "sparse_attn_route: at most 6144 key blocks per row for the Sol rule");
+  } else {
+    if (p->map_kblock < p->kblock || p->map_kblock % p->kblock || dims->Lkv % p->map_kblock)
+      return fail(SA_E_VALUE, "sparse_attn_route: map_kblock (%d) must be a multiple of kblock dividing Lkv", p->map_kblock);
+  }
+  if (G > 0) {
+    if (!k_centroid || !v_centroid || !count) return fail(SA_E_NULL, "sparse_attn_route: centroid outputs are required when G > 0");
+    if (!aligned16(k_centroid) || !aligned16(v_centroid)) return fail(SA_E_ALIGN, "sparse_attn_route: centroids must be 16-byte aligned");
+    if (const int32_t rc = check_v(v_dtype, v, v_scale, dims, p)) return rc;
+  }
+  size_t need = 0;
+  if (sol) {
+    need = sa::route_workspace_bytes(dims->B, dims->H, dims->Lq / 128, dims->Lkv / p->kblock, dims->d);
+    if (!workspace || workspace_bytes < need)
+      return fail(SA_E_WORKSPACE, "sparse_attn_route: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(SA_E_ALIGN, "sparse_attn_route: workspace must be 256-byte aligned");
+  }
+  if (const int32_t rc = check_current_device()) return rc;
+  if (dims->Lq == 0 || dims->Lkv == 0) return ok();
+  sa::RouteArgs a{};
+  a.q = q; a.k = k; a.k_scale = k_scale; a.v = v; a.v_int8 = v_dtype == SA_INT8; a.v_scale = v_scale;
+  a.v_block_src = v_block_src;
+  a.B = dims->B; a.H = dims->H; a.Lq = dims->Lq; a.Lkv = dims->Lkv; a.Lv = dims->Lv; a.d = dims->d;
+  a.lq_valid = dims->lq_valid; a.lkv_valid = dims->lkv_valid;
+  a.nQB = dims->Lq / 128; a.nKB = dims->Lkv / p->kblock; a.kblock = p->kblock; a.G = G;
+  a.prefix = p->prefix_tokens; a.k_scale_rows = p->k_scale_rows; a.v_scale_rows = p->v_scale_rows;
+  a.map_kblock = sol ? p->kblock : p->map_kblock; a.tau = p->threshold;
+  a.explicit_map = explicit_map; a.map = block_map; a.kc = k_centroid; a.vc = v_centroid; a.cnt = count;
+  a.stats = row_stats;
+  if (sol) {
+    char* ws = static_cast<char*>(workspace);
+    const size_t qbytes = ((size_t)a.B * a.H * a.nQB * a.d * 4 + 255) & ~(size_t)255;
+    a.qsum = reinterpret_cast<int32_t*>(ws);
+    a.ksum = reinterpret_cast<int32_t*>(ws + qbytes);
+  }
+  return launched(sa::launch_route(a, static_cast<hipStream_t>(stream)), "route");
+}
+
+int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale, const void* v,
+                        int32_t v_dtype, const float* v_scale, const int32_t* v_block_src, const sa_dims* dims,
+                        const sa_route_params* p, const uint8_t* block_map, const float* k_centroid,
+                        const float* v_centroid, const float* count, float sm_scale, void* out, int32_t out_dtype,
+                        float* lse, void* stream) {
+  if (const int32_t rc = check_dims(dims, p, v_block_src != nullptr)) return rc;
+  if (!q || !q_scale || !k || !k_scale || !block_map || !out)
+    return fail(SA_E_NULL, "sparse_attn_fwd: q, q_scale, k, k_scale, block_map and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(out)) return fail(SA_E_ALIGN, "sparse_attn_fwd: q, k and out must be 16-byte aligned");
+  if (const int32_t rc = check_v(v_dtype, v, v_scale, dims, p)) return rc;
+  if (out_dtype != SA_F32 && out_dtype != SA_BF16) return fail(SA_E_VALUE, "sparse_attn_fwd: out_dtype must be SA_F32 or SA_BF16");
+  if (!(sm_scale > 0.0f) || isinf(sm_scale)) return fail(SA_E_VALUE, "sparse_attn_fwd: sm_scale must be positive and finite");
+  if (p->centroids_per_block > 0) {
+    if (!k_centroid || !v_centroid || !count) return fail(SA_E_NULL, "sparse_attn_fwd: centroids are required when G > 0");
+    if (!aligned16(k_centroid) || !aligned16(v_centroid)) return fail(SA_E_ALIGN, "sparse_attn_fwd: centroids must be 16-byte aligned");
+  }
+  if (dims->Lkv % p->kblock) return fail(SA_E_SHAPE, "sparse_attn_fwd: Lkv must be a multiple of kblock");
+  if (const int32_t rc = check_current_device()) return rc;
+  if (dims->Lq == 0) return ok();
+  sa::FwdArgs a{};
+  a.q = q; a.q_scale = q_scale; a.k = k; a.k_scale = k_scale; a.v = v; a.v_scale = v_scale; a.v_block_src = v_block_src;
+  a.map = block_map; a.kc = k_centroid; a.vc = v_centroid; a.cnt = count; a.out = out; a.lse = lse;
+  a.B = dims->B; a.H = dims->H; a.Lq = dims->Lq; a.Lkv = dims->Lkv; a.Lv = dims->Lv; a.d = dims->d;
+  a.lq_valid = dims->lq_valid; a.lkv_valid = dims->lkv_valid;
+  a.nQB = dims->Lq / 128; a.nKB = dims->Lkv / p->kblock; a.kblock = p->kblock; a.G = p->centroids_per_block;
+  a.k_scale_rows = p->k_scale_rows; a.v_scale_rows = p->v_scale_rows;
+  a.v_int8 = v_dtype == SA_INT8; a.out_bf16 = out_dtype == SA_BF16;
+  a.sm_log2 = sm_scale * 1.4426950408889634f;
+  if ((int64_t)a.B * a.H * a.nQB > 0x7FFFFFFF) return fail(SA_E_SHAPE, "sparse_attn_fwd: too many query blocks");
+  return launched(sa::launch_fwd(a, static_cast<hipStream_t>(stream)), "fwd");
+}
+
+int32_t gather_virtual_kv(const void* k_phys_bf16, int32_t B, int32_t H, int32_t rows_per_slice, int32_t n_phys,
+                          int32_t d, const int32_t* src_map_host, int32_t n_logical, const float* rope_cos,
+                          const float* rope_sin, int32_t rot_offset, int32_t d_rot, int32_t k_rows_per_block,
+                          int8_t* k_logical, float* k_scale, int32_t* v_block_src, void* stream) {
+  if (!k_phys_bf16 || !src_map_host || !k_logical || !k_scale || !v_block_src)
+    return fail(SA_E_NULL, "gather_virtual_kv: k_phys, src_map_host, k_logical, k_scale and v_block_src are required");
+  if (B < 1 || H < 1 || n_phys < 1 || rows_per_slice < 1) return fail(SA_E_SHAPE, "gather_virtual_kv: bad sizes");
+  if (d != 64 && d != 128) return fail(SA_E_SHAPE, "gather_virtual_kv: d must be 64 or 128 (got %d)", d);
+  if (n_logical < 1 || n_logical > sa::kMaxLogical)
+    return fail(SA_E_SHAPE, "gather_virtual_kv: n_logical must be in [1, %d] (got %d)", sa::kMaxLogical, n_logical);
+  if (k_rows_per_block != 64 && k_rows_per_block != 128)
+    return fail(SA_E_VALUE, "gather_virtual_kv: k_rows_per_block must be 64 or 128");
+  if (rows_per_slice % k_rows_per_block || rows_per_slice % 64)
+    return fail(SA_E_SHAPE, "gather_virtual_kv: rows_per_slice must be a multiple of 64 and of k_rows_per_block");
+  if (d_rot < 0 || d_rot % 2 || rot_offset < 0 || rot_offset % 2 || rot_offset + d_rot > d)
+    return fail(SA_E_VALUE, "gather_virtual_kv: need even rot_offset and d_rot with rot_offset + d_rot <= d");
+  if (d_rot > 0 && (!rope_cos || !rope_sin)) return fail(SA_E_NULL, "gather_virtual_kv: rope tables are required");
+  if (!aligned16(k_phys_bf16) || !aligned16(k_logical)) return fail(SA_E_ALIGN, "gather_virtual_kv: k tensors must be 16-byte aligned");
+  sa::SrcMap sm{};
+  for (int l = 0; l < n_logical; ++l) {
+    if (src_map_host[l] < 0 || src_map_host[l] >= n_phys)
+      return fail(SA_E_VALUE, "gather_virtual_kv: src_map[%d] = %d outside [0, %d)", l, src_map_host[l], n_phys);
+    sm.v[l] = src_map_host[l];
+  }
+  if (const int32_t rc = check_current_device()) return rc;
+  sa::GatherArgs a{static_cast<const uint16_t*>(k_phys_bf16), B, H, rows_per_slice, n_phys, d, n_logical, rot_offset,
+                   d_rot, k_rows_per_block, sm, rope_cos, rope_sin, k_logical, k_scale, v_block_src};
+  return launched(sa::launch_gather(a, static_cast<hipStream_t>(stream)), "gather_virtual_kv");
+}
+
+}  // extern "C"

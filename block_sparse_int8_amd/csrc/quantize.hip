@@ -1,0 +1,155 @@
+// Per-block symmetric INT8 quantization and the virtual-KV gather (gfx950).
+//
+// Both kernels are HBM-bound streams: one workgroup owns one quantization block
+// (64 or 128 rows x d channels), keeps the whole block in registers (16-byte
+// loads, 8 bf16 per load), reduces amax across the workgroup, and writes the
+// INT8 codes with 8-byte stores — one read and one write of every element.
+//
+// Quantization rule (Configure Sol Sparse Attention, "How it works": Q and K are
+// prequantized to INT8 and those codes serve routing and the exact path;
+// FlashVSR Kitchen Sparse Attention, opening section: INT8 cache in 128-row
+// slabs): scale = amax/127; code = clamp(rint(x * (127/amax)), -127, 127) with
+// IEEE float32 division, one multiply and round-half-even; an all-zero block has
+// scale 0; rows at or past the valid length get code 0 and are left out of amax.
+#include "sa_device.h"
+#include "sa_launch.h"
+
+namespace sa {
+
+template <int D, int R>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t sB,
+                                                       int64_t sH, int64_t sL, int H, int L,
+                                                       int valid_len, int8_t* __restrict__ q,
+                                                       float* __restrict__ scale) {
+  constexpr int VPR = D / 8;            // 16-byte vectors per row
+  constexpr int NV = R * VPR / 256;     // vectors per thread
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const uint16_t* xb = x + b * sB + h * sH;
+  float vals[NV][8];
+  bool valid[NV];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = t + 256 * i, row = blk * R + v / VPR, cc = v % VPR;
+    valid[i] = row < valid_len;
+    const uint4 raw = *reinterpret_cast<const uint4*>(xb + row * sL + cc * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vals[i][2 * e] = __uint_as_float(w[e] << 16);
+      vals[i][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+    if (valid[i]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(vals[i][e]));
+    }
+  }
+  __shared__ float red[4];
+  amax = wave_max(amax);
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  const int nblk = L / R;
+  if (t == 0) scale[((int64_t)b * H + h) * nblk + blk] = amax / 127.0f;
+  int8_t* qb = q + ((int64_t)b * H + h) * L * D;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = t + 256 * i, row = blk * R + v / VPR, cc = v % VPR;
+    *reinterpret_cast<uint64_t*>(qb + (int64_t)row * D + cc * 8) = quant8(vals[i], inv, valid[i]);
+  }
+}
+
+// Virtual-KV gather (Configure H3 Static Virtual KV, mode list, "fast"): logical
+// row r of slice l reads physical slice src[l]; channel pairs inside the rotary
+// span are rotated by slice l's phase with y0 = fma(x0, c, -(x1*s)),
+// y1 = fma(x0, s, x1*c) in float32, rounded to bf16, then quantized per R
+// logical rows exactly as quantize_kernel does.  Nothing else is materialized.
+template <int D, int R>
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ kp, int H, int S,
+                                                     int n_phys, SrcMap src, const float* __restrict__ cosv,
+                                                     const float* __restrict__ sinv, int rot_offset,
+                                                     int d_rot, int n_logical, int8_t* __restrict__ kq,
+                                                     float* __restrict__ kscale, int32_t* __restrict__ vbs) {
+  constexpr int VPR = D / 8;
+  constexpr int NV = R * VPR / 256;
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int row0 = blk * R, l = row0 / S, npairs = d_rot / 2;
+  const int Lp = S * n_phys, Ll = S * n_logical;
+  const uint16_t* base = kp + (((int64_t)b * H + h) * Lp + (int64_t)src.v[l] * S + (row0 - l * S)) * D;
+  float vals[NV][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = t + 256 * i, r = v / VPR, cc = v % VPR;
+    const uint4 raw = *reinterpret_cast<const uint4*>(base + (int64_t)r * D + cc * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
+      const int c0 = cc * 8 + 2 * e;   // rot_offset is even, so pairs never straddle
+      if (c0 >= rot_offset && c0 < rot_offset + d_rot) {
+        const int pidx = l * npairs + (c0 - rot_offset) / 2;
+        const float cs = cosv[pidx], sn = sinv[pidx];
+        const float t1 = x1 * sn, t2 = x1 * cs;
+        const float y0 = __builtin_fmaf(x0, cs, -t1);
+        const float y1 = __builtin_fmaf(x0, sn, t2);
+        x0 = bf16_to_f32(f32_to_bf16_rne(y0));
+        x1 = bf16_to_f32(f32_to_bf16_rne(y1));
+      }
+      vals[i][2 * e] = x0;
+      vals[i][2 * e + 1] = x1;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(vals[i][e]));
+  }
+  __shared__ float red[4];
+  amax = wave_max(amax);
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  if (t == 0) kscale[((int64_t)b * H + h) * (Ll / R) + blk] = amax / 127.0f;
+  int8_t* qb = kq + (((int64_t)b * H + h) * Ll + row0) * D;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = t + 256 * i, r = v / VPR, cc = v % VPR;
+    *reinterpret_cast<uint64_t*>(qb + (int64_t)r * D + cc * 8) = quant8(vals[i], inv, true);
+  }
+  if (b == 0 && h == 0 && t < R / 64) {
+    const int bps = S / 64, j = row0 / 64 + t;
+    vbs[j] = src.v[l] * bps + j % bps;
+  }
+}
+
+template <int D>
+static hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t st) {
+  dim3 grid(a.L / a.R, a.H, a.B);
+  if (a.R == 64)
+    quantize_kernel<D, 64><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.L, a.valid_len, a.q, a.scale);
+  else
+    quantize_kernel<D, 128><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.L, a.valid_len, a.q, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st) {
+  return a.d == 64 ? launch_quantize_d<64>(a, st) : launch_quantize_d<128>(a, st);
+}
+
+template <int D>
+static hipError_t launch_gather_d(const GatherArgs& a, hipStream_t st) {
+  dim3 grid(a.n_logical * a.S / a.R, a.H, a.B);
+  if (a.R == 64)
+    gather_kernel<D, 64><<<grid, 256, 0, st>>>(a.kp, a.H, a.S, a.n_phys, a.src, a.cosv, a.sinv, a.rot_offset,
+                                               a.d_rot, a.n_logical, a.kq, a.kscale, a.vbs);
+  else
+    gather_kernel<D, 128><<<grid, 256, 0, st>>>(a.kp, a.H, a.S, a.n_phys, a.src, a.cosv, a.sinv, a.rot_offset,
+                                                a.d_rot, a.n_logical, a.kq, a.kscale, a.vbs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st) {
+  return a.d == 64 ? launch_gather_d<64>(a, st) : launch_gather_d<128>(a, st);
+}
+
+}  // namespace sa

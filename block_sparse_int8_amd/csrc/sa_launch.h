@@ -1,0 +1,85 @@
+// Internal launch interface between the C ABI layer (abi.hip) and the kernels.
+// Every struct carries already-validated arguments; launchers only enqueue.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kQBlock = 128;     // query rows per routing block
+constexpr int kTile = 64;        // key rows per exact tile in the forward kernel
+constexpr int kMaxLogical = 16;  // virtual-KV logical slices passed by value
+
+struct SrcMap {
+  int32_t v[kMaxLogical];
+};
+
+struct QuantizeArgs {
+  const uint16_t* x;
+  int64_t sB, sH, sL;
+  int B, H, L, d, valid_len, R;
+  int8_t* q;
+  float* scale;
+};
+
+struct GatherArgs {
+  const uint16_t* kp;
+  int B, H, S, n_phys, d, n_logical, rot_offset, d_rot, R;
+  SrcMap src;
+  const float* cosv;
+  const float* sinv;
+  int8_t* kq;
+  float* kscale;
+  int32_t* vbs;
+};
+
+struct RouteArgs {
+  const int8_t* q;
+  const int8_t* k;
+  const float* k_scale;
+  const void* v;
+  bool v_int8;
+  const float* v_scale;
+  const int32_t* v_block_src;
+  int B, H, Lq, Lkv, Lv, d, lq_valid, lkv_valid;
+  int nQB, nKB, kblock, G, prefix, k_scale_rows, v_scale_rows, map_kblock;
+  float tau;
+  const uint8_t* explicit_map;
+  uint8_t* map;
+  float* kc;
+  float* vc;
+  float* cnt;
+  double* stats;
+  int32_t* qsum;   // workspace [B,H,nQB,d] (Sol rule only)
+  int32_t* ksum;   // workspace [B,H,nKB,d] (Sol rule only)
+};
+
+struct FwdArgs {
+  const int8_t* q;
+  const float* q_scale;
+  const int8_t* k;
+  const float* k_scale;
+  const void* v;
+  const float* v_scale;
+  const int32_t* v_block_src;
+  const uint8_t* map;
+  const float* kc;
+  const float* vc;
+  const float* cnt;
+  void* out;
+  float* lse;
+  int B, H, Lq, Lkv, Lv, d, lq_valid, lkv_valid;
+  int nQB, nKB, kblock, G, k_scale_rows, v_scale_rows;
+  bool v_int8, out_bf16;
+  float sm_log2;   // sm_scale * log2(e)
+};
+
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
+
+// Route workspace layout: qsum then ksum, each 256-byte aligned.
+size_t route_workspace_bytes(int B, int H, int nQB, int nKB, int d);
+
+}  // namespace sa
