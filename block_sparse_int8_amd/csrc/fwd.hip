@@ -28,31 +28,28 @@
 #include "sa_device.h"
 #include "sa_launch.h"
 
+#include <limits.h>
+
 namespace sa {
 
 namespace {
 
-constexpr int kWin = 512;   // map entries scanned per list-building window
+constexpr int kWin = 512;      // map entries scanned per list-building window
+constexpr float kLazy = 8.0f;  // rescale O only when the row max grows by more than 2^8
 
 template <int D>
 struct FwdLds {
   static constexpr int KSTR = D + 16;         // int8 K tile row stride (bytes)
   static constexpr int VSTR = 2 * D + 64;     // bf16 V tile row stride (bytes)
   static constexpr int KCSTR = 2 * D + 16;    // bf16 centroid-K row stride (bytes)
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + kTile * KSTR;
-  static constexpr int TILE_END = V_OFF + kTile * VSTR;
-  static constexpr int KCH_OFF = 0;
-  static constexpr int KCL_OFF = KCH_OFF + 32 * KCSTR;
-  static constexpr int VCH_OFF = KCL_OFF + 32 * KCSTR;
-  static constexpr int VCL_OFF = VCH_OFF + 32 * VSTR;
-  static constexpr int CENT_END = VCL_OFF + 32 * VSTR;
-  static constexpr int DATA = (TILE_END > CENT_END ? TILE_END : CENT_END);
-  static constexpr int BIAS_OFF = DATA;                   // float[32]
-  static constexpr int ELIST_OFF = BIAS_OFF + 32 * 4;     // uint16[2*kWin]
-  static constexpr int CLIST_OFF = ELIST_OFF + 2 * kWin * 2;  // uint16[kWin]
-  static constexpr int CNT_OFF = CLIST_OFF + kWin * 2;    // int[2]
-  static constexpr int TOTAL = CNT_OFF + 16;
+  static constexpr int KU = KSTR / 16;        // 16-byte units per K row (last one padding)
+  static constexpr int VU = VSTR / 16;        // 16-byte units per V row (last four padding)
+  static constexpr int V_OFF = kTile * KSTR;
+  static constexpr int STAGE = V_OFF + kTile * VSTR;   // one pipeline stage: K tile + V tile
+  // centroid staging: K hi/lo in stage 0, V hi/lo in stage 1
+  static constexpr int KCL_OFF = 32 * KCSTR;
+  static constexpr int VCL_OFF = 32 * VSTR;
+  static_assert(2 * 32 * KCSTR <= STAGE && 2 * 32 * VSTR <= STAGE, "centroid staging must fit a stage");
 };
 
 __device__ __forceinline__ v4bf tr16(const uint8_t* lds_byte_ptr) {
@@ -75,33 +72,221 @@ __device__ __forceinline__ v8bf i8x8_to_bf16(int lo, int hi) {
   return r;
 }
 
+// max of a value over the lane pair (l, l^32), which hold the same query row.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
-// Online-softmax update for CNT scores per lane (log2 units).  The two lanes
-// l and l^32 hold the same query row, so the tile max is exchanged between
-// them; each lane keeps its own partial row sum.  On return x holds the
-// unnormalized probabilities exp2(x - m).
-template <int CNT, int NS>
-__device__ __forceinline__ void softmax_update(float (&x)[CNT], float& m_run, float& l_run, v16f (&O)[NS]) {
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < CNT; ++e) mloc = fmaxf(mloc, x[e]);
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-  const float m_new = fmaxf(m_run, mloc);
-  const float msub = m_new == -INFINITY ? 0.0f : m_new;
-  if (m_new > m_run) {
-    const float alpha = __builtin_amdgcn_exp2f(m_run - msub);
+// Lazy online-softmax rescale: the running max m_run only moves when a tile's
+// max exceeds it by more than kLazy (so exp2(x - m_run) <= 2^kLazy, safe in
+// bf16 and fp32); the wave takes the branch if any of its rows needs it.
+template <int NS>
+__device__ __forceinline__ void maybe_rescale(float m_tile, float& m_run, float& l_run, v16f (&O)[NS]) {
+  const bool need = m_tile > m_run + kLazy;
+  if (__ballot(need)) {
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
+    if (need) m_run = m_tile;
     l_run *= alpha;
 #pragma unroll
     for (int c = 0; c < NS; ++c) O[c] *= alpha;
-    m_run = m_new;
   }
-  float lsum = 0.0f;
+}
+
+// Direct global->LDS copy of one 64-row K tile (int8) and, unless V arrives as
+// INT8, one 64-row V tile (bf16) with global_load_lds_dwordx4.  Lane L of a
+// wave instruction lands at LDS offset 16*L of that instruction's 1 KiB chunk,
+// so the padded row layout is produced by picking each lane's source; padding
+// units re-read the row's last chunk.  The per-lane source offsets do not
+// depend on the tile and are computed once; the tile base is wave-uniform.
+template <int D>
+struct DmaPlan {
+  static constexpr int KI = (FwdLds<D>::KU + 3) / 4;   // K instructions per wave (at most)
+  static constexpr int VI = (FwdLds<D>::VU + 3) / 4;   // V instructions per wave (at most)
+  int koff[KI];
+  int voff[VI];
+};
+
+template <int D>
+__device__ __forceinline__ DmaPlan<D> make_dma_plan(int wave, int lane) {
+  using L = FwdLds<D>;
+  DmaPlan<D> pl;
 #pragma unroll
-  for (int e = 0; e < CNT; ++e) {
-    x[e] = __builtin_amdgcn_exp2f(x[e] - msub);
-    lsum += x[e];
+  for (int t = 0; t < DmaPlan<D>::KI; ++t) {
+    const int u = (wave + 4 * t) * 64 + lane, row = u / L::KU, c = min(u % L::KU, D / 16 - 1);
+    pl.koff[t] = row * D + c * 16;
   }
-  l_run += lsum;
+#pragma unroll
+  for (int t = 0; t < DmaPlan<D>::VI; ++t) {
+    const int u = (wave + 4 * t) * 64 + lane, row = u / L::VU, c = min(u % L::VU, 2 * D / 16 - 1);
+    pl.voff[t] = row * 2 * D + c * 16;
+  }
+  return pl;
+}
+
+// INT8 V (FlashVSR's INT8 cache) goes through registers so it can be widened
+// to bf16 exactly before it is written to LDS.
+template <int D>
+struct VRegs {
+  v4i r[D / 64];
+};
+
+template <int D>
+__device__ __forceinline__ void load_v_int8(const int8_t* vsrc, VRegs<D>& vr, int tid) {
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) {
+    const int v = tid + 256 * e, r = v / (D / 16), cc = v % (D / 16);
+    vr.r[e] = *reinterpret_cast<const v4i*>(vsrc + r * D + cc * 16);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_v_int8(uint8_t* buf, const VRegs<D>& vr, int tid) {
+  using L = FwdLds<D>;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) {
+    const int v = tid + 256 * e, r = v / (D / 16), cc = v % (D / 16);
+    *reinterpret_cast<v8bf*>(buf + L::V_OFF + r * L::VSTR + cc * 32) = i8x8_to_bf16(vr.r[e][0], vr.r[e][1]);
+    *reinterpret_cast<v8bf*>(buf + L::V_OFF + r * L::VSTR + cc * 32 + 16) = i8x8_to_bf16(vr.r[e][2], vr.r[e][3]);
+  }
+}
+
+// One exact 64-key tile from a staged buffer.
+//   S^T = K.Q^T on v_mfma_i32_32x32x32_i8 (exact int32); lane holds query row n
+//   and keys mb*32 + (i/4)*8 + hh*4 + i%4 of S^T block mb.
+//   Row max on the integers (scale c > 0 preserves order), then
+//   p = exp2(S*c - m_run) with c = a_i * b_j * sm_scale * log2(e): one FMA each.
+//   The row sum adds the bf16-rounded p (v_dot2 with (1,1)), i.e. exactly the
+//   weights the PV product uses.
+//   O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16.
+// MASKED is the tile holding the end of the valid keys (keys >= nvalid drop).
+template <int D, bool VI8, bool MASKED>
+__device__ __forceinline__ void exact_tile(const uint8_t* buf, const v4i (&qreg)[D / 32], v16f (&O)[D / 32],
+                                           float& m_run, float& l_run, float c, float pscale, int nvalid, int n,
+                                           int hh, int lane) {
+  using L = FwdLds<D>;
+  constexpr int NS = D / 32;
+  v16i acc0 = (v16i){}, acc1 = (v16i){};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const v4i k0 = *reinterpret_cast<const v4i*>(buf + n * L::KSTR + s * 32 + hh * 16);
+    const v4i k1 = *reinterpret_cast<const v4i*>(buf + (32 + n) * L::KSTR + s * 32 + hh * 16);
+    acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], acc1, 0, 0, 0);
+  }
+  int si[32];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    si[e] = acc0[e];
+    si[16 + e] = acc1[e];
+  }
+  if (MASKED) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int key = (e / 16) * 32 + ((e % 16) / 4) * 8 + hh * 4 + (e % 4);
+      if (key >= nvalid) si[e] = INT_MIN;
+    }
+  }
+  int mi = si[0];
+#pragma unroll
+  for (int e = 1; e < 31; e += 2) mi = max(mi, max(si[e], si[e + 1]));
+  mi = max(mi, si[31]);
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)mi, (unsigned)mi, false, false);
+    mi = max((int)r[0], (int)r[1]);
+  }
+  const float m_tile = (MASKED && mi == INT_MIN) ? -INFINITY : (float)mi * c;
+  maybe_rescale<NS>(m_tile, m_run, l_run, O);
+  const float neg = m_run == -INFINITY ? 0.0f : -m_run;
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  uint32_t pw[16];
+  float psum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si[2 * e], c, neg));
+    float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si[2 * e + 1], c, neg));
+    if (MASKED) {
+      p0 = si[2 * e] == INT_MIN ? 0.0f : p0;
+      p1 = si[2 * e + 1] == INT_MIN ? 0.0f : p1;
+    }
+    v2bf pk;
+    if (VI8) {
+      psum += p0 + p1;
+      pk = (v2bf){(__bf16)(p0 * pscale), (__bf16)(p1 * pscale)};
+    } else {
+      pk = (v2bf){(__bf16)p0, (__bf16)p1};
+      psum = __builtin_amdgcn_fdot2_f32_bf16(pk, (v2bf){(__bf16)1.0f, (__bf16)1.0f}, psum, false);
+    }
+    pw[e] = __builtin_bit_cast(uint32_t, pk);
+  }
+  l_run += psum;
+  const int g16 = lane >> 4, j16 = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const v4i pwv = (v4i){(int)pw[ks * 4], (int)pw[ks * 4 + 1], (int)pw[ks * 4 + 2], (int)pw[ks * 4 + 3]};
+    const v8bf pf = __builtin_bit_cast(v8bf, pwv);
+    const int krow = ks * 16 + hh * 4 + (j16 >> 2);
+#pragma unroll
+    for (int cb = 0; cb < NS; ++cb) {
+      const int col = cb * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
+      const uint8_t* p0 = buf + L::V_OFF + krow * L::VSTR + col * 2;
+      const v8bf vf = cat8(tr16(p0), tr16(p0 + 8 * L::VSTR));
+      O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[cb], 0, 0, 0);
+    }
+  }
+}
+
+// One 16-byte direct global->LDS load per lane (global_load_lds_dwordx4): the
+// lane's 16 bytes land at lds_chunk + 16 * lane.  Kept out of templates: the
+// host compilation pass only accepts the builtin in a plain function.
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_chunk) {
+  __builtin_amdgcn_global_load_lds(src, (SA_LDS void*)lds_chunk, 16, 0, 0);
+}
+
+// Scalars of one exact tile, loaded when its copy is issued (before the direct
+// loads) so the compute of the previous tile never waits on them.
+struct TileInfo {
+  int krow0, vrow0;
+  float kscale, pscale;   // raw loads: consumed only after the next barrier
+};
+
+template <bool VI8>
+__device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int kt, int nKS, int nVS) {
+  TileInfo t;
+  t.krow0 = kt * kTile;
+  t.vrow0 = t.krow0;
+  if (a.v_block_src)
+    t.vrow0 = __builtin_amdgcn_readfirstlane(min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile);
+  t.kscale = a.k_scale[bh * nKS + t.krow0 / a.k_scale_rows];
+  t.pscale = VI8 ? a.v_scale[bh * nVS + t.vrow0 / a.v_scale_rows] : 1.0f;
+  return t;
+}
+
+// Queue the copy of one tile into a stage: K (and bf16 V) by direct loads,
+// INT8 V into registers (written to LDS later by store_v_int8).
+template <int D, bool VI8>
+__device__ __forceinline__ void issue_tile(const TileInfo& t, uint8_t* buf, const int8_t* kbase,
+                                           const uint8_t* v16base, const int8_t* v8base, const DmaPlan<D>& plan,
+                                           VRegs<D>& vr, int wave, int tid) {
+  using L = FwdLds<D>;
+  const int8_t* ksrc = kbase + (int64_t)t.krow0 * D;
+#pragma unroll
+  for (int u = 0; u < DmaPlan<D>::KI; ++u) {
+    const int inst = wave + 4 * u;
+    if (inst < L::KU)
+      lds_dma16(ksrc + plan.koff[u], buf + inst * 1024);
+  }
+  if (VI8) {
+    load_v_int8<D>(v8base + (int64_t)t.vrow0 * D, vr, tid);
+  } else {
+    const uint8_t* vsrc = v16base + (int64_t)t.vrow0 * D * 2;
+#pragma unroll
+    for (int u = 0; u < DmaPlan<D>::VI; ++u) {
+      const int inst = wave + 4 * u;
+      if (inst < L::VU)
+        lds_dma16(vsrc + plan.voff[u], buf + L::V_OFF + inst * 1024);
+    }
+  }
 }
 
 }  // namespace
@@ -110,7 +295,14 @@ template <int D, bool VI8, bool OBF16>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using L = FwdLds<D>;
   constexpr int NS = D / 32;   // int8 k-steps of 32 channels; also 32-channel output blocks
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  // Two pipeline stages as separate LDS objects, so the compiler can see that
+  // reading one stage does not depend on the direct loads into the other.
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[L::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[L::STAGE];
+  __shared__ uint16_t elist[2 * kWin];
+  __shared__ uint16_t clist[kWin];
+  __shared__ float bias[32];
+  __shared__ int cnts[3];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hh = lane >> 5;
 
@@ -140,120 +332,90 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int c = 0; c < NS; ++c) O[c] = (v16f){};
   float m_run = -INFINITY, l_run = 0.0f;
-
-  uint16_t* elist = reinterpret_cast<uint16_t*>(lds + L::ELIST_OFF);
-  uint16_t* clist = reinterpret_cast<uint16_t*>(lds + L::CLIST_OFF);
-  int* cnts = reinterpret_cast<int*>(lds + L::CNT_OFF);
-  float* bias = reinterpret_cast<float*>(lds + L::BIAS_OFF);
   const uint8_t* mrow = a.map + (bh * a.nQB + i) * a.nKB;
+  const int8_t* kbase = a.k + bh * a.Lkv * D;
+  const int8_t* v8base = static_cast<const int8_t*>(a.v) + bh * a.Lv * D;
+  const uint8_t* v16base = static_cast<const uint8_t*>(a.v) + bh * a.Lv * D * 2;
+  VRegs<D> vr;
+  const DmaPlan<D> plan = make_dma_plan<D>(wave, lane);
 
   for (int w0 = 0; w0 < a.nKB; w0 += kWin) {
     const int wend = min(a.nKB, w0 + kWin);
     __syncthreads();
     if (wave == 0) {
-      int nE = 0, nC = 0;
+      // Exact tiles go to elist, except the one tile that holds the end of the
+      // valid keys (it needs masking and is done after the pipelined loop);
+      // tiles entirely past the valid keys are skipped.
+      int nE = 0, nC = 0, ptile = -1;
       const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       for (int c0 = w0; c0 < wend; c0 += 64) {
         const int j = c0 + lane;
         const int st = j < wend ? mrow[j] : 0;
         const bool isE = st == 1, isC = st == 2 && a.G > 0;
-        const uint64_t bE = __ballot(isE), bC = __ballot(isC);
+        int nf = 0;
         if (isE) {
-          const int pos = nE + __popcll(bE & lt);
-          for (int sub = 0; sub < tpb; ++sub) elist[pos * tpb + sub] = (uint16_t)((j - w0) * tpb + sub);
+          for (int sub = 0; sub < tpb; ++sub) {
+            const int tr0 = (j * tpb + sub) * kTile;
+            if (tr0 + kTile <= a.lkv_valid) ++nf;
+            else if (tr0 < a.lkv_valid) ptile = j * tpb + sub;
+          }
+        }
+        const uint64_t b0 = __ballot(nf & 1), b1 = __ballot(nf & 2), bC = __ballot(isC);
+        if (nf) {
+          int pos = nE + __popcll(b0 & lt) + 2 * __popcll(b1 & lt);
+          for (int sub = 0; sub < tpb; ++sub) {
+            const int tr0 = (j * tpb + sub) * kTile;
+            if (tr0 + kTile <= a.lkv_valid) elist[pos++] = (uint16_t)((j - w0) * tpb + sub);
+          }
         }
         if (isC) clist[nC + __popcll(bC & lt)] = (uint16_t)(j - w0);
-        nE += __popcll(bE);
+        nE += __popcll(b0) + 2 * __popcll(b1);
         nC += __popcll(bC);
       }
+      const uint64_t bp = __ballot(ptile >= 0);
       if (lane == 0) {
-        cnts[0] = nE * tpb;
+        cnts[0] = nE;
         cnts[1] = nC;
+        cnts[2] = -1;
       }
+      if (bp && lane == __builtin_ctzll(bp)) cnts[2] = ptile;
     }
     __syncthreads();
-    const int nE = cnts[0], nC = cnts[1];
+    const int nE = cnts[0], nC = cnts[1], ptile = cnts[2];
 
-    // ---------------- exact 64-key tiles ----------------
-    for (int e = 0; e < nE; ++e) {
-      const int kt = w0 * tpb + elist[e];     // global 64-key tile index
-      const int krow0 = kt * kTile;
-      int vrow0 = krow0;
-      if (a.v_block_src) {
-        int pb = a.v_block_src[kt];
-        pb = min(max(pb, 0), a.Lv / kTile - 1);
-        vrow0 = pb * kTile;
-      }
-      // stage K (int8) and V (bf16; INT8 V is widened exactly) into LDS
-      {
-        const int8_t* ks = a.k + (bh * a.Lkv + krow0) * D;
-        for (int v = tid; v < kTile * D / 16; v += 256) {
-          const int r = v / (D / 16), cc = v % (D / 16);
-          *reinterpret_cast<uint4*>(lds + L::K_OFF + r * L::KSTR + cc * 16) =
-              *reinterpret_cast<const uint4*>(ks + r * D + cc * 16);
+    // ---------------- exact 64-key tiles, two-stage pipeline ----------------
+    if (nE > 0) {
+      TileInfo cur = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS), nxt = cur;
+      issue_tile<D, VI8>(cur, stage0, kbase, v16base, v8base, plan, vr, wave, tid);
+      if (VI8) store_v_int8<D>(stage0, vr, tid);
+      for (int e = 0; e < nE; e += 2) {
+        __syncthreads();                         // tile e is in stage0; stage1 is free
+        if (e + 1 < nE) {
+          nxt = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 1]), nKS, nVS);
+          issue_tile<D, VI8>(nxt, stage1, kbase, v16base, v8base, plan, vr, wave, tid);
         }
-        if (VI8) {
-          const int8_t* vs = static_cast<const int8_t*>(a.v) + (bh * a.Lv + vrow0) * D;
-          for (int v = tid; v < kTile * D / 16; v += 256) {
-            const int r = v / (D / 16), cc = v % (D / 16);
-            const v4i raw = *reinterpret_cast<const v4i*>(vs + r * D + cc * 16);
-            *reinterpret_cast<v8bf*>(lds + L::V_OFF + r * L::VSTR + cc * 32) = i8x8_to_bf16(raw[0], raw[1]);
-            *reinterpret_cast<v8bf*>(lds + L::V_OFF + r * L::VSTR + cc * 32 + 16) = i8x8_to_bf16(raw[2], raw[3]);
-          }
-        } else {
-          const uint16_t* vs = static_cast<const uint16_t*>(a.v) + (bh * a.Lv + vrow0) * D;
-          for (int v = tid; v < kTile * D / 8; v += 256) {
-            const int r = v / (D / 8), cc = v % (D / 8);
-            *reinterpret_cast<uint4*>(lds + L::V_OFF + r * L::VSTR + cc * 16) =
-                *reinterpret_cast<const uint4*>(vs + r * D + cc * 8);
-          }
+        exact_tile<D, VI8, false>(stage0, qreg, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, n, hh, lane);
+        if (e + 1 >= nE) break;
+        if (VI8) store_v_int8<D>(stage1, vr, tid);
+        cur = nxt;
+        __syncthreads();                         // tile e+1 is in stage1; stage0 is free
+        if (e + 2 < nE) {
+          nxt = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 2]), nKS, nVS);
+          issue_tile<D, VI8>(nxt, stage0, kbase, v16base, v8base, plan, vr, wave, tid);
         }
+        exact_tile<D, VI8, false>(stage1, qreg, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, n, hh, lane);
+        if (VI8 && e + 2 < nE) store_v_int8<D>(stage0, vr, tid);
+        cur = nxt;
       }
+    }
+    __syncthreads();                             // stages free again
+    if (ptile >= 0) {                            // the tile with the end of the valid keys
+      const TileInfo t = fetch_tile<VI8>(a, bh, ptile, nKS, nVS);
+      issue_tile<D, VI8>(t, stage0, kbase, v16base, v8base, plan, vr, wave, tid);
+      if (VI8) store_v_int8<D>(stage0, vr, tid);
       __syncthreads();
-
-      // S^T = K . Q^T  (two 32-key halves)
-      v16i acc0 = (v16i){}, acc1 = (v16i){};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const v4i k0 = *reinterpret_cast<const v4i*>(lds + L::K_OFF + n * L::KSTR + s * 32 + hh * 16);
-        const v4i k1 = *reinterpret_cast<const v4i*>(lds + L::K_OFF + (32 + n) * L::KSTR + s * 32 + hh * 16);
-        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], acc1, 0, 0, 0);
-      }
-      const float c = qc * a.k_scale[bh * nKS + krow0 / a.k_scale_rows];
-      float x[32];
-#pragma unroll
-      for (int e2 = 0; e2 < 16; ++e2) {
-        x[e2] = (float)acc0[e2] * c;
-        x[16 + e2] = (float)acc1[e2] * c;
-      }
-      if (krow0 + kTile > a.lkv_valid) {
-#pragma unroll
-        for (int e2 = 0; e2 < 32; ++e2) {
-          const int key = krow0 + (e2 / 16) * 32 + ((e2 % 16) / 4) * 8 + hh * 4 + (e2 % 4);
-          if (key >= a.lkv_valid) x[e2] = -INFINITY;
-        }
-      }
-      softmax_update<32, NS>(x, m_run, l_run, O);
-      float pscale = 1.0f;
-      if (VI8) pscale = a.v_scale[bh * nVS + vrow0 / a.v_scale_rows];
-
-      // O^T += V^T . P^T  (four 16-key steps)
-      const int g16 = lane >> 4, j16 = lane & 15;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        v8bf pf;
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) pf[e2] = (__bf16)(x[ks * 8 + e2] * pscale);
-        const int krow = ks * 16 + hh * 4 + (j16 >> 2);
-#pragma unroll
-        for (int cb = 0; cb < NS; ++cb) {
-          const int col = cb * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
-          const uint8_t* p0 = lds + L::V_OFF + krow * L::VSTR + col * 2;
-          const v8bf vf = cat8(tr16(p0), tr16(p0 + 8 * L::VSTR));
-          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[cb], 0, 0, 0);
-        }
-      }
+      exact_tile<D, VI8, true>(stage0, qreg, O, m_run, l_run, qc * t.kscale, t.pscale, a.lkv_valid - t.krow0, n,
+                               hh, lane);
       __syncthreads();
     }
 
@@ -283,10 +445,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           vhi[e2] = (__bf16)vf[e2];
           vlo[e2] = (__bf16)(vf[e2] - (float)vhi[e2]);
         }
-        *reinterpret_cast<v4bf*>(lds + L::KCH_OFF + col * L::KCSTR + c4 * 8) = khi;
-        *reinterpret_cast<v4bf*>(lds + L::KCL_OFF + col * L::KCSTR + c4 * 8) = klo;
-        *reinterpret_cast<v4bf*>(lds + L::VCH_OFF + col * L::VSTR + c4 * 8) = vhi;
-        *reinterpret_cast<v4bf*>(lds + L::VCL_OFF + col * L::VSTR + c4 * 8) = vlo;
+        *reinterpret_cast<v4bf*>(stage0 + col * L::KCSTR + c4 * 8) = khi;
+        *reinterpret_cast<v4bf*>(stage0 + L::KCL_OFF + col * L::KCSTR + c4 * 8) = klo;
+        *reinterpret_cast<v4bf*>(stage1 + col * L::VSTR + c4 * 8) = vhi;
+        *reinterpret_cast<v4bf*>(stage1 + L::VCL_OFF + col * L::VSTR + c4 * 8) = vlo;
         if (c4 == 0) bias[col] = cn > 0.0f ? __log2f(cn) : -INFINITY;
       }
       __syncthreads();
@@ -297,19 +459,30 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int pp = 0; pp < 2; ++pp) {
           const v8bf qb = i8x8_to_bf16(qreg[s][2 * pp], qreg[s][2 * pp + 1]);
           const int off = n * L::KCSTR + (s * 32 + hh * 16 + pp * 8) * 2;
-          const v8bf khi = *reinterpret_cast<const v8bf*>(lds + L::KCH_OFF + off);
-          const v8bf klo = *reinterpret_cast<const v8bf*>(lds + L::KCL_OFF + off);
+          const v8bf khi = *reinterpret_cast<const v8bf*>(stage0 + off);
+          const v8bf klo = *reinterpret_cast<const v8bf*>(stage0 + L::KCL_OFF + off);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb, acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qb, acc, 0, 0, 0);
         }
       }
       float x[16];
+      float mx = -INFINITY;
 #pragma unroll
       for (int e2 = 0; e2 < 16; ++e2) {
         const int col = (e2 / 4) * 8 + hh * 4 + (e2 % 4);
-        x[e2] = acc[e2] * qc + bias[col];
+        x[e2] = __builtin_fmaf(acc[e2], qc, bias[col]);
+        mx = fmaxf(mx, x[e2]);
       }
-      softmax_update<16, NS>(x, m_run, l_run, O);
+      mx = pair_max(mx);
+      maybe_rescale<NS>(mx, m_run, l_run, O);
+      const float msub = m_run == -INFINITY ? 0.0f : m_run;
+      float psum = 0.0f;
+#pragma unroll
+      for (int e2 = 0; e2 < 16; ++e2) {
+        x[e2] = __builtin_amdgcn_exp2f(x[e2] - msub);
+        psum += x[e2];
+      }
+      l_run += psum;
       const int g16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -320,8 +493,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NS; ++cb) {
           const int col = cb * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
-          const uint8_t* ph = lds + L::VCH_OFF + krow * L::VSTR + col * 2;
-          const uint8_t* pl = lds + L::VCL_OFF + krow * L::VSTR + col * 2;
+          const uint8_t* ph = stage1 + krow * L::VSTR + col * 2;
+          const uint8_t* pl = stage1 + L::VCL_OFF + krow * L::VSTR + col * 2;
           const v8bf vh = cat8(tr16(ph), tr16(ph + 8 * L::VSTR));
           const v8bf vl = cat8(tr16(pl), tr16(pl + 8 * L::VSTR));
           O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pf, O[cb], 0, 0, 0);
@@ -360,10 +533,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
 template <int D, bool VI8>
 static hipError_t launch_fwd_dv(const FwdArgs& a, hipStream_t st) {
-  const size_t lds = FwdLds<D>::TOTAL;
   dim3 grid(a.B * a.H * a.nQB);
-  if (a.out_bf16) fwd_kernel<D, VI8, true><<<grid, 256, lds, st>>>(a);
-  else fwd_kernel<D, VI8, false><<<grid, 256, lds, st>>>(a);
+  if (a.out_bf16) fwd_kernel<D, VI8, true><<<grid, 256, 0, st>>>(a);
+  else fwd_kernel<D, VI8, false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -52,7 +52,9 @@ def _check_workload(orc, wl, tau=None, sel=None, out_dtype=torch.float32, tol=(M
     mx, mean, rows = compare_outputs(g["out"], o["out"], o["sel"], nQB, wl.Lq, wl.lq_valid, skip)
     say(f"  out: rows {rows}, max-abs {mx:.3e}, mean-abs {mean:.3e}, blocks skipped for ties {len(skip)}")
     assert mx <= tol[0] and mean <= tol[1]
-    # lse on valid rows
+    # lse on valid rows.  The kernel's row sum adds the bf16-rounded weights it
+    # also uses for PV, each within 2^-9 (relative) of the exact weight, so
+    # |lse - lse_exact| <= ln(1 + 2^-9) ~= 1.95e-3 plus fp32 rounding.
     B_H = wl.B * wl.H
     gl = g["lse"].reshape(B_H, wl.Lq)
     for e, sid in enumerate(np.asarray(o["sel"])):
@@ -63,7 +65,7 @@ def _check_workload(orc, wl, tau=None, sel=None, out_dtype=torch.float32, tol=(M
         fin = np.isfinite(ol)
         assert np.array_equal(np.isfinite(gl[bh, i * 128:(i + 1) * 128]), fin)
         if fin.any():
-            assert np.abs(gl[bh, i * 128:(i + 1) * 128][fin] - ol[fin]).max() < 1e-3
+            assert np.abs(gl[bh, i * 128:(i + 1) * 128][fin] - ol[fin]).max() < 2.5e-3
     return g, o
 
 
