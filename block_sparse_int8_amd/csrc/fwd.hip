@@ -151,63 +151,34 @@ __device__ __forceinline__ void store_v_int8(uint8_t* buf, const VRegs<D>& vr, i
   }
 }
 
-// One exact 64-key tile from a staged buffer.
-//   S^T = K.Q^T on v_mfma_i32_32x32x32_i8 (exact int32); lane holds query row n
-//   and keys mb*32 + (i/4)*8 + hh*4 + i%4 of S^T block mb.
-//   Row max on the integers (scale c > 0 preserves order), then
-//   p = exp2(S*c - m_run) with c = a_i * b_j * sm_scale * log2(e): one FMA each.
-//   The row sum adds the bf16-rounded p (v_dot2 with (1,1)), i.e. exactly the
-//   weights the PV product uses.
-//   O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16.
-// MASKED is the tile holding the end of the valid keys (keys >= nvalid drop).
-template <int D, bool VI8, bool MASKED>
-__device__ __forceinline__ void exact_tile(const uint8_t* buf, const v4i (&qreg)[D / 32], v16f (&O)[D / 32],
-                                           float& m_run, float& l_run, float c, float pscale, int nvalid, int n,
-                                           int hh, int lane) {
-  using L = FwdLds<D>;
-  constexpr int NS = D / 32;
-  v16i acc0 = (v16i){}, acc1 = (v16i){};
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const v4i k0 = *reinterpret_cast<const v4i*>(buf + n * L::KSTR + s * 32 + hh * 16);
-    const v4i k1 = *reinterpret_cast<const v4i*>(buf + (32 + n) * L::KSTR + s * 32 + hh * 16);
-    acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], acc1, 0, 0, 0);
-  }
-  int si[32];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    si[e] = acc0[e];
-    si[16 + e] = acc1[e];
-  }
-  if (MASKED) {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int key = (e / 16) * 32 + ((e % 16) / 4) * 8 + hh * 4 + (e % 4);
-      if (key >= nvalid) si[e] = INT_MIN;
-    }
-  }
-  int mi = si[0];
-#pragma unroll
-  for (int e = 1; e < 31; e += 2) mi = max(mi, max(si[e], si[e + 1]));
-  mi = max(mi, si[31]);
-  {
-    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)mi, (unsigned)mi, false, false);
-    mi = max((int)r[0], (int)r[1]);
-  }
-  const float m_tile = (MASKED && mi == INT_MIN) ? -INFINITY : (float)mi * c;
-  maybe_rescale<NS>(m_tile, m_run, l_run, O);
-  const float neg = m_run == -INFINITY ? 0.0f : -m_run;
+// Scores leave the integer MFMA already in float form: the accumulators start
+// at the bit pattern of 1.5 * 2^23, whose float spacing is 1, so the finished
+// int32 accumulator read as a float is exactly 1.5 * 2^23 + S while
+// |S| < 2^21 (|S| <= 127 * 127 * d < 2^21 for d <= 128).
+constexpr int kMagicI = 0x4B400000;
+constexpr float kMagicF = 12582912.0f;
+// Fast-path acceptance bound on a lane's partial row sum (each weight is at
+// most this, so every weight stays far from fp32/bf16 overflow).
+constexpr float kFastSum = 4096.0f;
+
+// p = exp2(S*c - m) for the 16 scores a lane holds in one 32-key half of the
+// tile, as bf16 pairs (INT8 V: scaled by the V block scale before rounding).
+// x = 1.5*2^23 + S, and b = -(1.5*2^23*c + m) is formed once per row, so each
+// weight is one FMA and one exp2.  Returns the lane's row-sum part: the
+// bf16-rounded weights (bf16 V) or the unrounded unscaled ones (INT8 V).
+template <bool VI8, bool MASKED>
+__device__ __forceinline__ float half_weights(const v16i& acc, int key0, float c, float b, float pscale, int nvalid,
+                                              int hh, uint32_t (&pw)[8]) {
   typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  uint32_t pw[16];
   float psum = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si[2 * e], c, neg));
-    float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si[2 * e + 1], c, neg));
+  for (int e = 0; e < 8; ++e) {
+    float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[2 * e]), c, b));
+    float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[2 * e + 1]), c, b));
     if (MASKED) {
-      p0 = si[2 * e] == INT_MIN ? 0.0f : p0;
-      p1 = si[2 * e + 1] == INT_MIN ? 0.0f : p1;
+      const int k0 = key0 + ((2 * e) / 4) * 8 + hh * 4 + (2 * e) % 4;
+      p0 = k0 < nvalid ? p0 : 0.0f;
+      p1 = k0 + 1 < nvalid ? p1 : 0.0f;
     }
     v2bf pk;
     if (VI8) {
@@ -219,21 +190,188 @@ __device__ __forceinline__ void exact_tile(const uint8_t* buf, const v4i (&qreg)
     }
     pw[e] = __builtin_bit_cast(uint32_t, pk);
   }
-  l_run += psum;
+  return psum;
+}
+
+// Row max over a half's scores in score*c units (the lane pair l, l^32 holds
+// one query row); -inf when none of them is valid.
+template <bool MASKED>
+__device__ __forceinline__ float half_max(const v16i& acc, int key0, float c, int nvalid, int hh) {
+  int mi = INT_MIN;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    int v = acc[e];
+    if (MASKED) v = key0 + (e / 4) * 8 + hh * 4 + (e % 4) < nvalid ? v : INT_MIN;
+    mi = max(mi, v);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)mi, (unsigned)mi, false, false);
+  mi = max((int)r[0], (int)r[1]);
+  return mi == INT_MIN ? -INFINITY : (float)(mi - kMagicI) * c;
+}
+
+// Exact online-softmax step for one 32-key half: the half's row max moves
+// m_run lazily, then the weights are computed against it.  Returns the lane's
+// row-sum part.
+template <int NS, bool VI8, bool MASKED>
+__device__ __forceinline__ float half_exact(const v16i& acc, int key0, float c, float pscale, int nvalid, int hh,
+                                            v16f (&O)[NS], float& m_run, float& l_run, uint32_t (&pw)[8]) {
+  maybe_rescale<NS>(half_max<MASKED>(acc, key0, c, nvalid, hh), m_run, l_run, O);
+  // rows with no valid key so far keep m_run = -inf; their weights are 0
+  const float m = m_run == -INFINITY ? 0.0f : m_run;
+  return half_weights<VI8, MASKED>(acc, key0, c, -__builtin_fmaf(kMagicF, c, m), pscale, nvalid, hh, pw);
+}
+
+// Fast-path acceptance: every lane's partial row sum is finite and at most
+// kFastSum.  With m_run = -inf (no step yet) the weights are +inf and fail.
+__device__ __forceinline__ bool fast_ok(float psum) { return __ballot(!(psum <= kFastSum)) == 0; }
+
+// O^T += V^T.P^T for one 32-key half (two k-steps of 16 keys).
+template <int D>
+__device__ __forceinline__ void half_pv(const uint8_t* vbuf, int key0, const uint32_t (&pw)[8], v16f (&O)[D / 32],
+                                        int hh, int lane) {
+  using L = FwdLds<D>;
   const int g16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const v4i pwv = (v4i){(int)pw[ks * 4], (int)pw[ks * 4 + 1], (int)pw[ks * 4 + 2], (int)pw[ks * 4 + 3]};
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const v4i pwv = (v4i){(int)pw[k2 * 4], (int)pw[k2 * 4 + 1], (int)pw[k2 * 4 + 2], (int)pw[k2 * 4 + 3]};
     const v8bf pf = __builtin_bit_cast(v8bf, pwv);
-    const int krow = ks * 16 + hh * 4 + (j16 >> 2);
+    const int krow = key0 + k2 * 16 + hh * 4 + (j16 >> 2);
 #pragma unroll
-    for (int cb = 0; cb < NS; ++cb) {
+    for (int cb = 0; cb < D / 32; ++cb) {
       const int col = cb * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
-      const uint8_t* p0 = buf + L::V_OFF + krow * L::VSTR + col * 2;
+      const uint8_t* p0 = vbuf + krow * L::VSTR + col * 2;
       const v8bf vf = cat8(tr16(p0), tr16(p0 + 8 * L::VSTR));
       O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[cb], 0, 0, 0);
     }
   }
+}
+
+// One exact 64-key tile from a staged buffer, as two 32-key halves.
+//   S^T = K.Q^T on v_mfma_i32_32x32x32_i8 (exact int32); in half h the lane
+//   holds query row n and keys 32h + (i/4)*8 + hh*4 + i%4.
+//   c = a_i * b_j * sm_scale * log2(e); weights p = exp2(S*c - m_run).
+//   The halves are separate online-softmax steps, ordered so that the softmax
+//   of one half can run on the vector ALU while the matrix core works on the
+//   other: QK(h0), QK(h1) | softmax(h0) | PV(h0) | softmax(h1) | PV(h1).
+//   The row sum adds the bf16-rounded p (v_dot2 with (1,1)), i.e. exactly the
+//   weights the PV product uses.
+//   O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16.
+// MASKED is the tile holding the end of the valid keys (keys >= nvalid drop).
+// One weight pair (scores 2e, 2e+1 of a half) on the fast path: two FMAs, two
+// exp2, one bf16 pack and the row-sum update.
+template <bool VI8>
+__device__ __forceinline__ void weight_pair(const v16i& acc, int e, float c, float b, float pscale, float& psum,
+                                            uint32_t (&pw)[8]) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[2 * e]), c, b));
+  const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[2 * e + 1]), c, b));
+  v2bf pk;
+  if (VI8) {
+    psum += p0 + p1;
+    pk = (v2bf){(__bf16)(p0 * pscale), (__bf16)(p1 * pscale)};
+  } else {
+    pk = (v2bf){(__bf16)p0, (__bf16)p1};
+    psum = __builtin_amdgcn_fdot2_f32_bf16(pk, (v2bf){(__bf16)1.0f, (__bf16)1.0f}, psum, false);
+  }
+  pw[e] = __builtin_bit_cast(uint32_t, pk);
+}
+
+// V^T operand of PV MFMA i (k-step i / NS of the half, output block i % NS).
+template <int D>
+__device__ __forceinline__ v8bf v_frag(const uint8_t* vbuf, int key0, int i, int hh, int lane) {
+  using L = FwdLds<D>;
+  constexpr int NS = D / 32;
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int krow = key0 + (i / NS) * 16 + hh * 4 + (j16 >> 2);
+  const int col = (i % NS) * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
+  const uint8_t* p0 = vbuf + krow * L::VSTR + col * 2;
+  return cat8(tr16(p0), tr16(p0 + 8 * L::VSTR));
+}
+
+template <int D>
+__device__ __forceinline__ v8bf p_frag(const uint32_t (&pw)[8], int i) {
+  constexpr int NS = D / 32;
+  const int k2 = i / NS;
+  const v4i pwv = (v4i){(int)pw[k2 * 4], (int)pw[k2 * 4 + 1], (int)pw[k2 * 4 + 2], (int)pw[k2 * 4 + 3]};
+  return __builtin_bit_cast(v8bf, pwv);
+}
+
+// One exact 64-key tile from a staged buffer, as two 32-key halves.
+//   S^T = K.Q^T on v_mfma_i32_32x32x32_i8 (exact int32); in half h the lane
+//   holds query row n and keys 32h + (i/4)*8 + hh*4 + i%4.
+//   c = a_i * b_j * sm_scale * log2(e); weights p = exp2(S*c - m_run).
+//   The halves are separate online-softmax steps.  Each one first computes
+//   its weights against m_run as it stands and keeps them when every lane's
+//   partial row sum is finite and at most kFastSum; otherwise (the first step,
+//   a jump in the scores) the exact step recomputes them after moving m_run.
+//   A wave issues in order, so the weight work is interleaved by hand with
+//   independent matrix-core work: the weights of half 0 with the QK MFMAs of
+//   half 1, the weights of half 1 with the PV MFMAs of half 0 (one MFMA, then
+//   one or two weight pairs, in fixed scheduling segments).
+//   The row sum adds the bf16-rounded p (v_dot2 with (1,1)), i.e. exactly the
+//   weights the PV product uses.
+//   O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16.
+// MASKED is the tile holding the end of the valid keys (keys >= nvalid drop).
+template <int D, bool VI8, bool MASKED>
+__device__ __forceinline__ void exact_tile(const uint8_t* buf, const v4i (&qreg)[D / 32], const v16i& magic,
+                                           v16f (&O)[D / 32], float& m_run, float& l_run, float c, float pscale,
+                                           int nvalid, int n, int hh, int lane) {
+  using L = FwdLds<D>;
+  constexpr int NS = D / 32;
+  const uint8_t* vbuf = buf + L::V_OFF;
+  v4i k0[NS], k1[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    k0[s] = *reinterpret_cast<const v4i*>(buf + n * L::KSTR + s * 32 + hh * 16);
+    k1[s] = *reinterpret_cast<const v4i*>(buf + (32 + n) * L::KSTR + s * 32 + hh * 16);
+  }
+  v16i acc0 = magic, acc1 = magic;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[s], qreg[s], acc0, 0, 0, 0);
+  uint32_t pw0[8], pw1[8];
+  if (MASKED) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[s], qreg[s], acc1, 0, 0, 0);
+    l_run += half_exact<NS, VI8, true>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
+    half_pv<D>(vbuf, 0, pw0, O, hh, lane);
+    l_run += half_exact<NS, VI8, true>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
+    half_pv<D>(vbuf, 32, pw1, O, hh, lane);
+    return;
+  }
+  // QK of half 1, interleaved with the weights of half 0 (8 pairs).
+  float ps0 = 0.0f;
+  {
+    const float b = -__builtin_fmaf(kMagicF, c, m_run);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[s], qreg[s], acc1, 0, 0, 0);
+#pragma unroll
+      for (int e = s * (8 / NS); e < (s + 1) * (8 / NS); ++e) weight_pair<VI8>(acc0, e, c, b, pscale, ps0, pw0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (!fast_ok(ps0)) ps0 = half_exact<NS, VI8, false>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
+  l_run += ps0;
+  // PV of half 0 (2*NS MFMAs), interleaved with the weights of half 1.
+  float ps1 = 0.0f;
+  {
+    const float b = -__builtin_fmaf(kMagicF, c, m_run);
+    v8bf vf = v_frag<D>(vbuf, 0, 0, hh, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NS; ++i) {
+      const v8bf vn = v_frag<D>(vbuf, 0, i + 1 < 2 * NS ? i + 1 : i, hh, lane);
+      O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_frag<D>(pw0, i), O[i % NS], 0, 0, 0);
+#pragma unroll
+      for (int e = i * 8 / (2 * NS); e < (i + 1) * 8 / (2 * NS); ++e) weight_pair<VI8>(acc1, e, c, b, pscale, ps1, pw1);
+      vf = vn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (!fast_ok(ps1)) ps1 = half_exact<NS, VI8, false>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
+  l_run += ps1;
+  half_pv<D>(vbuf, 32, pw1, O, hh, lane);
 }
 
 // One 16-byte direct global->LDS load per lane (global_load_lds_dwordx4): the
@@ -328,6 +466,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
   const float qc = a.q_scale[bh * a.nQB + i] * a.sm_log2;
 
+  // Initial value of the integer score accumulators (see kMagicI), built once:
+  // the empty asm keeps it in registers instead of re-creating it per tile.
+  v16i magic;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) magic[e] = kMagicI;
+  asm volatile("" : "+v"(magic));
   v16f O[NS];
 #pragma unroll
   for (int c = 0; c < NS; ++c) O[c] = (v16f){};
@@ -394,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           nxt = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 1]), nKS, nVS);
           issue_tile<D, VI8>(nxt, stage1, kbase, v16base, v8base, plan, vr, wave, tid);
         }
-        exact_tile<D, VI8, false>(stage0, qreg, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, n, hh, lane);
+        exact_tile<D, VI8, false>(stage0, qreg, magic, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, n, hh, lane);
         if (e + 1 >= nE) break;
         if (VI8) store_v_int8<D>(stage1, vr, tid);
         cur = nxt;
@@ -403,7 +547,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           nxt = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 2]), nKS, nVS);
           issue_tile<D, VI8>(nxt, stage0, kbase, v16base, v8base, plan, vr, wave, tid);
         }
-        exact_tile<D, VI8, false>(stage1, qreg, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, n, hh, lane);
+        exact_tile<D, VI8, false>(stage1, qreg, magic, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, n, hh, lane);
         if (VI8 && e + 2 < nE) store_v_int8<D>(stage0, vr, tid);
         cur = nxt;
       }
@@ -414,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       issue_tile<D, VI8>(t, stage0, kbase, v16base, v8base, plan, vr, wave, tid);
       if (VI8) store_v_int8<D>(stage0, vr, tid);
       __syncthreads();
-      exact_tile<D, VI8, true>(stage0, qreg, O, m_run, l_run, qc * t.kscale, t.pscale, a.lkv_valid - t.krow0, n,
+      exact_tile<D, VI8, true>(stage0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, a.lkv_valid - t.krow0, n,
                                hh, lane);
       __syncthreads();
     }
