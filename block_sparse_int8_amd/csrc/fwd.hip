@@ -61,6 +61,16 @@ __device__ __forceinline__ v8bf cat8(v4bf a, v4bf b) {
   return (v8bf){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// A lane offset passed through an empty asm statement: LDS addresses are then
+// formed as stage + offset + constant, a derivation short enough for the
+// compiler to keep track of which LDS variable each read touches (it only
+// follows a few pointer steps).  Without that knowledge it would make every
+// such read wait for all direct LDS copies in flight.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // 8 int8 codes (two dwords) -> 8 bf16 (exact: |code| <= 127).
 __device__ __forceinline__ v8bf i8x8_to_bf16(int lo, int hi) {
   v8bf r;
@@ -93,19 +103,23 @@ __device__ __forceinline__ void maybe_rescale(float m_tile, float& m_run, float&
   }
 }
 
-// Direct global->LDS copy of one 64-row K tile (int8) and, unless V arrives as
-// INT8, one 64-row V tile (bf16) with global_load_lds_dwordx4.  Lane L of a
-// wave instruction lands at LDS offset 16*L of that instruction's 1 KiB chunk,
-// so the padded row layout is produced by picking each lane's source; padding
-// units re-read the row's last chunk.  The per-lane source offsets do not
-// depend on the tile and are computed once; the tile base is wave-uniform.
+// Direct copy into LDS of one 64-row K tile (int8) and, unless V arrives as
+// INT8, one 64-row V tile (bf16) with buffer_load_dwordx4 ... lds.  Lane L of
+// a wave instruction lands at LDS offset 16*L of that instruction's 1 KiB
+// chunk, so the padded row layout is produced by picking each lane's source;
+// lanes on padding fetch nothing (kPadOffset).  The per-lane source offsets do
+// not depend on the tile and are computed once; the tile offset is a scalar.
 template <int D>
 struct DmaPlan {
   static constexpr int KI = (FwdLds<D>::KU + 3) / 4;   // K instructions per wave (at most)
   static constexpr int VI = (FwdLds<D>::VU + 3) / 4;   // V instructions per wave (at most)
-  int koff[KI];
-  int voff[VI];
+  uint32_t koff[KI];   // unsigned: the copy uses a scalar base plus a 32-bit lane offset
+  uint32_t voff[VI];
 };
+
+// Lanes that land on a row's padding get an offset past any buffer's end:
+// the buffer load returns zeros for them without touching memory.
+constexpr uint32_t kPadOffset = 0xFFFFFFF0u;
 
 template <int D>
 __device__ __forceinline__ DmaPlan<D> make_dma_plan(int wave, int lane) {
@@ -113,13 +127,13 @@ __device__ __forceinline__ DmaPlan<D> make_dma_plan(int wave, int lane) {
   DmaPlan<D> pl;
 #pragma unroll
   for (int t = 0; t < DmaPlan<D>::KI; ++t) {
-    const int u = (wave + 4 * t) * 64 + lane, row = u / L::KU, c = min(u % L::KU, D / 16 - 1);
-    pl.koff[t] = row * D + c * 16;
+    const int u = (wave + 4 * t) * 64 + lane, row = u / L::KU, c = u % L::KU;
+    pl.koff[t] = c < D / 16 ? (uint32_t)(row * D + c * 16) : kPadOffset;
   }
 #pragma unroll
   for (int t = 0; t < DmaPlan<D>::VI; ++t) {
-    const int u = (wave + 4 * t) * 64 + lane, row = u / L::VU, c = min(u % L::VU, 2 * D / 16 - 1);
-    pl.voff[t] = row * 2 * D + c * 16;
+    const int u = (wave + 4 * t) * 64 + lane, row = u / L::VU, c = u % L::VU;
+    pl.voff[t] = c < 2 * D / 16 ? (uint32_t)(row * 2 * D + c * 16) : kPadOffset;
   }
   return pl;
 }
@@ -149,6 +163,93 @@ __device__ __forceinline__ void store_v_int8(uint8_t* buf, const VRegs<D>& vr, i
     *reinterpret_cast<v8bf*>(buf + L::V_OFF + r * L::VSTR + cc * 32) = i8x8_to_bf16(vr.r[e][0], vr.r[e][1]);
     *reinterpret_cast<v8bf*>(buf + L::V_OFF + r * L::VSTR + cc * 32 + 16) = i8x8_to_bf16(vr.r[e][2], vr.r[e][3]);
   }
+}
+
+// One 16-byte direct load per lane into LDS (buffer_load_dwordx4 ... lds):
+// the lane's 16 bytes, at byte voff + soff of the buffer, land at LDS byte
+// address lds_addr + 16 * lane.  The buffer form takes a scalar base and a
+// 32-bit lane offset that does not change from tile to tile, so a copy costs
+// no vector instructions; loads past the buffer's end return zeros.  The LDS
+// address is passed as a plain wave-uniform integer that the compiler cannot
+// trace to an LDS variable: it then keeps the copy in order with every LDS
+// access but adds no wait of its own for it before later LDS reads.  The tile
+// loop's barriers wait for the copies (vmcnt(0) before each __syncthreads),
+// and no LDS read touches a stage while its copy is in flight.  Kept out of
+// templates: the host compilation pass only accepts the builtin in a plain
+// function.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                          uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("" : "+s"(lds_addr));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SA_LDS void*)(uintptr_t)lds_addr, 16, voff, soff, 0, 0);
+}
+
+// Buffer resource over num_bytes at base (raw, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(SA_LDS const void*)p;
+}
+
+// Scalars of one exact tile, loaded when its copy is issued (before the direct
+// loads) so the compute of the previous tile never waits on them.
+struct TileInfo {
+  int krow0, vrow0;
+  float kscale, pscale;   // raw loads: consumed only after the next barrier
+};
+
+template <bool VI8>
+__device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int kt, int nKS, int nVS) {
+  TileInfo t;
+  t.krow0 = kt * kTile;
+  t.vrow0 = t.krow0;
+  if (a.v_block_src)
+    t.vrow0 = __builtin_amdgcn_readfirstlane(min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile);
+  t.kscale = a.k_scale[bh * nKS + t.krow0 / a.k_scale_rows];
+  t.pscale = VI8 ? a.v_scale[bh * nVS + t.vrow0 / a.v_scale_rows] : 1.0f;
+  return t;
+}
+
+// The copy of one tile into a stage, issued piecewise: K (and bf16 V) by
+// direct loads, INT8 V into registers (written to LDS later by store_v_int8).
+// A wave owns K instructions wave + 4u (u < KI) and V instructions wave + 4u
+// (u < VI).  The tile loop hands this to the compute of the current tile,
+// which issues the pieces between its matrix-core segments: issued in one
+// burst, the copies of all waves on a CU queue behind each other in the
+// vector-memory path and stall the waves' in-order issue.
+template <int D, bool VI8>
+struct TileCopy {
+  __amdgpu_buffer_rsrc_t krs, vrs;   // K (int8) and bf16 V of this head
+  uint32_t koff, voff;               // byte offsets of the tile's first K / V row
+  uint32_t lds;                      // destination stage (LDS byte address)
+  const DmaPlan<D>* plan;
+  int wave;
+  bool active;                       // false: nothing to copy
+  __device__ __forceinline__ void k(int u) const {
+    const int inst = wave + 4 * u;
+    if (active && u < DmaPlan<D>::KI && inst < FwdLds<D>::KU) lds_dma16(krs, plan->koff[u], koff, lds + inst * 1024);
+  }
+  __device__ __forceinline__ void v(int u) const {
+    const int inst = wave + 4 * u;
+    if (!VI8 && active && u < DmaPlan<D>::VI && inst < FwdLds<D>::VU)
+      lds_dma16(vrs, plan->voff[u], voff, lds + FwdLds<D>::V_OFF + inst * 1024);
+  }
+  __device__ __forceinline__ void all() const {
+#pragma unroll
+    for (int u = 0; u < DmaPlan<D>::KI; ++u) k(u);
+#pragma unroll
+    for (int u = 0; u < DmaPlan<D>::VI; ++u) v(u);
+  }
+};
+
+template <int D, bool VI8>
+__device__ __forceinline__ TileCopy<D, VI8> tile_copy(const TileInfo& t, uint8_t* buf, __amdgpu_buffer_rsrc_t krs,
+                                                      __amdgpu_buffer_rsrc_t vrs, const DmaPlan<D>& plan, int wave,
+                                                      bool active) {
+  return TileCopy<D, VI8>{krs, vrs, (uint32_t)(t.krow0 * D), (uint32_t)(t.vrow0 * D * 2), lds_address(buf), &plan,
+                          wave, active};
 }
 
 // Scores leave the integer MFMA already in float form: the accumulators start
@@ -228,35 +329,8 @@ __device__ __forceinline__ bool fast_ok(float psum) { return __ballot(!(psum <= 
 // O^T += V^T.P^T for one 32-key half (two k-steps of 16 keys).
 template <int D>
 __device__ __forceinline__ void half_pv(const uint8_t* vbuf, int key0, const uint32_t (&pw)[8], v16f (&O)[D / 32],
-                                        int hh, int lane) {
-  using L = FwdLds<D>;
-  const int g16 = lane >> 4, j16 = lane & 15;
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    const v4i pwv = (v4i){(int)pw[k2 * 4], (int)pw[k2 * 4 + 1], (int)pw[k2 * 4 + 2], (int)pw[k2 * 4 + 3]};
-    const v8bf pf = __builtin_bit_cast(v8bf, pwv);
-    const int krow = key0 + k2 * 16 + hh * 4 + (j16 >> 2);
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) {
-      const int col = cb * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
-      const uint8_t* p0 = vbuf + krow * L::VSTR + col * 2;
-      const v8bf vf = cat8(tr16(p0), tr16(p0 + 8 * L::VSTR));
-      O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[cb], 0, 0, 0);
-    }
-  }
-}
+                                        int vlane);
 
-// One exact 64-key tile from a staged buffer, as two 32-key halves.
-//   S^T = K.Q^T on v_mfma_i32_32x32x32_i8 (exact int32); in half h the lane
-//   holds query row n and keys 32h + (i/4)*8 + hh*4 + i%4.
-//   c = a_i * b_j * sm_scale * log2(e); weights p = exp2(S*c - m_run).
-//   The halves are separate online-softmax steps, ordered so that the softmax
-//   of one half can run on the vector ALU while the matrix core works on the
-//   other: QK(h0), QK(h1) | softmax(h0) | PV(h0) | softmax(h1) | PV(h1).
-//   The row sum adds the bf16-rounded p (v_dot2 with (1,1)), i.e. exactly the
-//   weights the PV product uses.
-//   O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16.
-// MASKED is the tile holding the end of the valid keys (keys >= nvalid drop).
 // One weight pair (scores 2e, 2e+1 of a half) on the fast path: two FMAs, two
 // exp2, one bf16 pack and the row-sum update.
 template <bool VI8>
@@ -277,14 +351,12 @@ __device__ __forceinline__ void weight_pair(const v16i& acc, int e, float c, flo
 }
 
 // V^T operand of PV MFMA i (k-step i / NS of the half, output block i % NS).
+// vlane: the lane's byte offset (hh*4 + j16/4) * VSTR + ((g16&1)*16 + 4*(j16&3)) * 2.
 template <int D>
-__device__ __forceinline__ v8bf v_frag(const uint8_t* vbuf, int key0, int i, int hh, int lane) {
+__device__ __forceinline__ v8bf v_frag(const uint8_t* vbuf, int key0, int i, int vlane) {
   using L = FwdLds<D>;
   constexpr int NS = D / 32;
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const int krow = key0 + (i / NS) * 16 + hh * 4 + (j16 >> 2);
-  const int col = (i % NS) * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
-  const uint8_t* p0 = vbuf + krow * L::VSTR + col * 2;
+  const uint8_t* p0 = vbuf + vlane + (key0 + (i / NS) * 16) * L::VSTR + (i % NS) * 64;
   return cat8(tr16(p0), tr16(p0 + 8 * L::VSTR));
 }
 
@@ -294,6 +366,16 @@ __device__ __forceinline__ v8bf p_frag(const uint32_t (&pw)[8], int i) {
   const int k2 = i / NS;
   const v4i pwv = (v4i){(int)pw[k2 * 4], (int)pw[k2 * 4 + 1], (int)pw[k2 * 4 + 2], (int)pw[k2 * 4 + 3]};
   return __builtin_bit_cast(v8bf, pwv);
+}
+
+template <int D>
+__device__ __forceinline__ void half_pv(const uint8_t* vbuf, int key0, const uint32_t (&pw)[8], v16f (&O)[D / 32],
+                                        int vlane) {
+  constexpr int NS = D / 32;
+#pragma unroll
+  for (int i = 0; i < 2 * NS; ++i)
+    O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(vbuf, key0, i, vlane), p_frag<D>(pw, i), O[i % NS],
+                                                        0, 0, 0);
 }
 
 // One exact 64-key tile from a staged buffer, as two 32-key halves.
@@ -315,27 +397,28 @@ __device__ __forceinline__ v8bf p_frag(const uint32_t (&pw)[8], int i) {
 template <int D, bool VI8, bool MASKED>
 __device__ __forceinline__ void exact_tile(const uint8_t* buf, const v4i (&qreg)[D / 32], const v16i& magic,
                                            v16f (&O)[D / 32], float& m_run, float& l_run, float c, float pscale,
-                                           int nvalid, int n, int hh, int lane) {
+                                           int nvalid, int klane, int vlane, int hh, const TileCopy<D, VI8>& cp) {
   using L = FwdLds<D>;
   constexpr int NS = D / 32;
   const uint8_t* vbuf = buf + L::V_OFF;
   v4i k0[NS], k1[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    k0[s] = *reinterpret_cast<const v4i*>(buf + n * L::KSTR + s * 32 + hh * 16);
-    k1[s] = *reinterpret_cast<const v4i*>(buf + (32 + n) * L::KSTR + s * 32 + hh * 16);
+    k0[s] = *reinterpret_cast<const v4i*>(buf + klane + s * 32);
+    k1[s] = *reinterpret_cast<const v4i*>(buf + klane + 32 * L::KSTR + s * 32);
   }
   v16i acc0 = magic, acc1 = magic;
 #pragma unroll
   for (int s = 0; s < NS; ++s) acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[s], qreg[s], acc0, 0, 0, 0);
   uint32_t pw0[8], pw1[8];
   if (MASKED) {
+    cp.all();
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[s], qreg[s], acc1, 0, 0, 0);
     l_run += half_exact<NS, VI8, true>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
-    half_pv<D>(vbuf, 0, pw0, O, hh, lane);
+    half_pv<D>(vbuf, 0, pw0, O, vlane);
     l_run += half_exact<NS, VI8, true>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
-    half_pv<D>(vbuf, 32, pw1, O, hh, lane);
+    half_pv<D>(vbuf, 32, pw1, O, vlane);
     return;
   }
   // QK of half 1, interleaved with the weights of half 0 (8 pairs).
@@ -346,10 +429,13 @@ __device__ __forceinline__ void exact_tile(const uint8_t* buf, const v4i (&qreg)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[s], qreg[s], acc1, 0, 0, 0);
+      cp.k(s);                                            // next tile's K copies
 #pragma unroll
       for (int e = s * (8 / NS); e < (s + 1) * (8 / NS); ++e) weight_pair<VI8>(acc0, e, c, b, pscale, ps0, pw0);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int u = NS; u < DmaPlan<D>::KI; ++u) cp.k(u);
   }
   if (!fast_ok(ps0)) ps0 = half_exact<NS, VI8, false>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
   l_run += ps0;
@@ -357,75 +443,26 @@ __device__ __forceinline__ void exact_tile(const uint8_t* buf, const v4i (&qreg)
   float ps1 = 0.0f;
   {
     const float b = -__builtin_fmaf(kMagicF, c, m_run);
-    v8bf vf = v_frag<D>(vbuf, 0, 0, hh, lane);
+    v8bf vf = v_frag<D>(vbuf, 0, 0, vlane);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2 * NS; ++i) {
-      const v8bf vn = v_frag<D>(vbuf, 0, i + 1 < 2 * NS ? i + 1 : i, hh, lane);
+      const v8bf vn = v_frag<D>(vbuf, 0, i + 1 < 2 * NS ? i + 1 : i, vlane);
       O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_frag<D>(pw0, i), O[i % NS], 0, 0, 0);
+      cp.v(i);                                            // next tile's V copies
 #pragma unroll
       for (int e = i * 8 / (2 * NS); e < (i + 1) * 8 / (2 * NS); ++e) weight_pair<VI8>(acc1, e, c, b, pscale, ps1, pw1);
       vf = vn;
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int u = 2 * NS; u < DmaPlan<D>::VI; ++u) cp.v(u);
   }
   if (!fast_ok(ps1)) ps1 = half_exact<NS, VI8, false>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
   l_run += ps1;
-  half_pv<D>(vbuf, 32, pw1, O, hh, lane);
+  half_pv<D>(vbuf, 32, pw1, O, vlane);
 }
 
-// One 16-byte direct global->LDS load per lane (global_load_lds_dwordx4): the
-// lane's 16 bytes land at lds_chunk + 16 * lane.  Kept out of templates: the
-// host compilation pass only accepts the builtin in a plain function.
-__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_chunk) {
-  __builtin_amdgcn_global_load_lds(src, (SA_LDS void*)lds_chunk, 16, 0, 0);
-}
-
-// Scalars of one exact tile, loaded when its copy is issued (before the direct
-// loads) so the compute of the previous tile never waits on them.
-struct TileInfo {
-  int krow0, vrow0;
-  float kscale, pscale;   // raw loads: consumed only after the next barrier
-};
-
-template <bool VI8>
-__device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int kt, int nKS, int nVS) {
-  TileInfo t;
-  t.krow0 = kt * kTile;
-  t.vrow0 = t.krow0;
-  if (a.v_block_src)
-    t.vrow0 = __builtin_amdgcn_readfirstlane(min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile);
-  t.kscale = a.k_scale[bh * nKS + t.krow0 / a.k_scale_rows];
-  t.pscale = VI8 ? a.v_scale[bh * nVS + t.vrow0 / a.v_scale_rows] : 1.0f;
-  return t;
-}
-
-// Queue the copy of one tile into a stage: K (and bf16 V) by direct loads,
-// INT8 V into registers (written to LDS later by store_v_int8).
-template <int D, bool VI8>
-__device__ __forceinline__ void issue_tile(const TileInfo& t, uint8_t* buf, const int8_t* kbase,
-                                           const uint8_t* v16base, const int8_t* v8base, const DmaPlan<D>& plan,
-                                           VRegs<D>& vr, int wave, int tid) {
-  using L = FwdLds<D>;
-  const int8_t* ksrc = kbase + (int64_t)t.krow0 * D;
-#pragma unroll
-  for (int u = 0; u < DmaPlan<D>::KI; ++u) {
-    const int inst = wave + 4 * u;
-    if (inst < L::KU)
-      lds_dma16(ksrc + plan.koff[u], buf + inst * 1024);
-  }
-  if (VI8) {
-    load_v_int8<D>(v8base + (int64_t)t.vrow0 * D, vr, tid);
-  } else {
-    const uint8_t* vsrc = v16base + (int64_t)t.vrow0 * D * 2;
-#pragma unroll
-    for (int u = 0; u < DmaPlan<D>::VI; ++u) {
-      const int inst = wave + 4 * u;
-      if (inst < L::VU)
-        lds_dma16(vsrc + plan.voff[u], buf + L::V_OFF + inst * 1024);
-    }
-  }
-}
 
 }  // namespace
 
@@ -443,6 +480,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ int cnts[3];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hh = lane >> 5;
+  // per-lane LDS byte offsets within a stage: K fragment (row n, channels
+  // hh*16..) and V^T fragment (see v_frag)
+  const int klane = opaque(n * L::KSTR + hh * 16);
+  const int vlane = opaque((hh * 4 + ((lane & 15) >> 2)) * L::VSTR + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2);
 
   // XCD-aware block order: hardware id b runs on XCD b % 8; give each XCD a
   // contiguous range of (head, query block) work items.
@@ -480,6 +521,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int8_t* kbase = a.k + bh * a.Lkv * D;
   const int8_t* v8base = static_cast<const int8_t*>(a.v) + bh * a.Lv * D;
   const uint8_t* v16base = static_cast<const uint8_t*>(a.v) + bh * a.Lv * D * 2;
+  // buffer resources over this head's K and bf16 V (the tile copies); the
+  // per-head sizes fit 32 bits (checked when the call is validated)
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kbase, (uint32_t)((int64_t)a.Lkv * D));
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v16base, VI8 ? 0u : (uint32_t)((int64_t)a.Lv * D * 2));
   VRegs<D> vr;
   const DmaPlan<D> plan = make_dma_plan<D>(wave, lane);
 
@@ -530,36 +575,42 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // ---------------- exact 64-key tiles, two-stage pipeline ----------------
     if (nE > 0) {
       TileInfo cur = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS), nxt = cur;
-      issue_tile<D, VI8>(cur, stage0, kbase, v16base, v8base, plan, vr, wave, tid);
+      if (VI8) load_v_int8<D>(v8base + (int64_t)cur.vrow0 * D, vr, tid);
+      tile_copy<D, VI8>(cur, stage0, krs, vrs, plan, wave, true).all();
       if (VI8) store_v_int8<D>(stage0, vr, tid);
       for (int e = 0; e < nE; e += 2) {
         __syncthreads();                         // tile e is in stage0; stage1 is free
-        if (e + 1 < nE) {
+        const bool more1 = e + 1 < nE;
+        if (more1) {
           nxt = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 1]), nKS, nVS);
-          issue_tile<D, VI8>(nxt, stage1, kbase, v16base, v8base, plan, vr, wave, tid);
+          if (VI8) load_v_int8<D>(v8base + (int64_t)nxt.vrow0 * D, vr, tid);
         }
-        exact_tile<D, VI8, false>(stage0, qreg, magic, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, n, hh, lane);
-        if (e + 1 >= nE) break;
+        exact_tile<D, VI8, false>(stage0, qreg, magic, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, klane, vlane, hh,
+                                  tile_copy<D, VI8>(nxt, stage1, krs, vrs, plan, wave, more1));
+        if (!more1) break;
         if (VI8) store_v_int8<D>(stage1, vr, tid);
         cur = nxt;
         __syncthreads();                         // tile e+1 is in stage1; stage0 is free
-        if (e + 2 < nE) {
+        const bool more2 = e + 2 < nE;
+        if (more2) {
           nxt = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 2]), nKS, nVS);
-          issue_tile<D, VI8>(nxt, stage0, kbase, v16base, v8base, plan, vr, wave, tid);
+          if (VI8) load_v_int8<D>(v8base + (int64_t)nxt.vrow0 * D, vr, tid);
         }
-        exact_tile<D, VI8, false>(stage1, qreg, magic, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, n, hh, lane);
-        if (VI8 && e + 2 < nE) store_v_int8<D>(stage0, vr, tid);
+        exact_tile<D, VI8, false>(stage1, qreg, magic, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, klane, vlane, hh,
+                                  tile_copy<D, VI8>(nxt, stage0, krs, vrs, plan, wave, more2));
+        if (VI8 && more2) store_v_int8<D>(stage0, vr, tid);
         cur = nxt;
       }
     }
     __syncthreads();                             // stages free again
     if (ptile >= 0) {                            // the tile with the end of the valid keys
       const TileInfo t = fetch_tile<VI8>(a, bh, ptile, nKS, nVS);
-      issue_tile<D, VI8>(t, stage0, kbase, v16base, v8base, plan, vr, wave, tid);
+      if (VI8) load_v_int8<D>(v8base + (int64_t)t.vrow0 * D, vr, tid);
+      tile_copy<D, VI8>(t, stage0, krs, vrs, plan, wave, true).all();
       if (VI8) store_v_int8<D>(stage0, vr, tid);
       __syncthreads();
-      exact_tile<D, VI8, true>(stage0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, a.lkv_valid - t.krow0, n,
-                               hh, lane);
+      exact_tile<D, VI8, true>(stage0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, a.lkv_valid - t.krow0,
+                               klane, vlane, hh, tile_copy<D, VI8>(t, stage1, krs, vrs, plan, wave, false));
       __syncthreads();
     }
 
