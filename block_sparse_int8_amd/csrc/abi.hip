@@ -202,9 +202,9 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
   a.stats = row_stats;
   if (sol) {
     char* ws = static_cast<char*>(workspace);
-    const size_t qbytes = ((size_t)a.B * a.H * a.nQB * a.d * 4 + 255) & ~(size_t)255;
-    a.qsum = reinterpret_cast<int32_t*>(ws);
-    a.ksum = reinterpret_cast<int32_t*>(ws + qbytes);
+    const size_t qbytes = ((size_t)a.B * a.H * a.nQB * 2 * a.d + 255) & ~(size_t)255;
+    a.qdig = reinterpret_cast<int8_t*>(ws);
+    a.kdig = reinterpret_cast<int8_t*>(ws + qbytes);
   }
   return launched(sa::launch_route(a, static_cast<hipStream_t>(stream)), "route");
 }

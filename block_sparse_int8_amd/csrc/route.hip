@@ -22,98 +22,166 @@
 
 namespace sa {
 
-// One workgroup per (query block, head, batch): stage the 128 x D codes in LDS,
-// then each thread sums one column over a half of the rows.
-template <int D>
-__global__ __launch_bounds__(256) void pool_q_kernel(const int8_t* __restrict__ q, int H, int Lq,
-                                                     int lq_valid, int nQB, int32_t* __restrict__ qsum) {
-  __shared__ __attribute__((aligned(16))) int8_t tile[kQBlock * D];
-  __shared__ int32_t part[2][D];
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  const int64_t bh = (int64_t)b * H + h;
-  const int8_t* src = q + (bh * Lq + (int64_t)i * kQBlock) * D;
-  constexpr int NV = kQBlock * D / 16 / 256;
-#pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    const int v = t + 256 * e;
-    reinterpret_cast<uint4*>(tile)[v] = reinterpret_cast<const uint4*>(src)[v];
+// Column sums straight from HBM: a lane owns one dword column (4 int8 codes, or
+// 2 bf16 values) of a block and every RG-th row of it; its loads are issued
+// before any is used, so each workgroup keeps the whole block in flight, and
+// the per-lane partial sums meet in LDS.  All rows of a block lie inside the
+// tensor (L is a multiple of the block size); rows past the valid length are
+// loaded and multiplied by zero.
+
+// Per-column sums of the 4 int8 codes in a dword, over the rows a lane owns.
+// u = w ^ 0x80808080 holds code + 128 (0..255) in each byte; bytes 0 and 2
+// accumulate in the 16-bit halves of lo, bytes 1 and 3 in those of hi, with
+// plain 32-bit adds (no carry crosses a half: at most 128 rows x 255 < 2^16),
+// and 128 per counted row is taken off at the end.  Five vector operations
+// per four codes.
+struct I8Cols {
+  uint32_t lo = 0, hi = 0;
+  int n = 0;
+  __device__ __forceinline__ void add(uint32_t w, bool valid) {
+    const uint32_t u = valid ? (w ^ 0x80808080u) : 0u;
+    lo += u & 0x00FF00FFu;
+    hi += (u >> 8) & 0x00FF00FFu;
+    n += valid ? 1 : 0;
   }
-  __syncthreads();
-  const int nvalid = min(kQBlock, max(0, lq_valid - i * kQBlock));
-  for (int w = t; w < 2 * D; w += 256) {
-    const int col = w % D, half = w / D;
-    int32_t s = 0;
-    for (int r = half * 64; r < half * 64 + 64 && r < nvalid; ++r) s += tile[r * D + col];
-    part[half][col] = s;
+  __device__ __forceinline__ int4 sums() const {
+    const int o = 128 * n;
+    return make_int4((int)(lo & 0xFFFFu) - o, (int)(hi & 0xFFFFu) - o, (int)(lo >> 16) - o, (int)(hi >> 16) - o);
   }
-  __syncthreads();
-  for (int col = t; col < D; col += 256) qsum[(bh * nQB + i) * D + col] = part[0][col] + part[1][col];
+};
+
+// A column sum x (|x| <= 127 * 128) as two int8 digits, x = 128 * hi + lo with
+// lo in [-64, 63] and |hi| <= 127, so the proxy products run on the int8
+// matrix cores.
+__device__ __forceinline__ void store_digits(int8_t* dst, int d, int col, int32_t x) {
+  const int32_t hi = (x + 64) >> 7;
+  dst[col] = (int8_t)hi;
+  dst[d + col] = (int8_t)(x - 128 * hi);
 }
 
-// One workgroup per (key block, head, batch).  Rows are summed per 32-row
-// chunk so that 2x32 groups, and groups that span two K scale blocks, combine
-// their chunks with the right scale.
-template <int D, bool VI8>
+// One workgroup per (query block, head, batch).
+template <int D>
+__global__ __launch_bounds__(256) void pool_q_kernel(const int8_t* __restrict__ q, int H, int Lq,
+                                                     int lq_valid, int nQB, int8_t* __restrict__ qdig) {
+  constexpr int DW = D / 4;              // dwords per row
+  constexpr int RG = 256 / DW;           // row groups
+  constexpr int NR = kQBlock / RG;       // rows per lane
+  __shared__ int32_t part[RG][D];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int dw = t % DW, rg = t / DW;
+  const int64_t bh = (int64_t)b * H + h;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(q + (bh * Lq + (int64_t)i * kQBlock) * D) + dw;
+  const int nvalid = min(kQBlock, max(0, lq_valid - i * kQBlock));
+  uint32_t w[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) w[k] = src[(rg + RG * k) * DW];
+  I8Cols acc;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) acc.add(w[k], rg + RG * k < nvalid);
+  *reinterpret_cast<int4*>(&part[rg][dw * 4]) = acc.sums();
+  __syncthreads();
+  for (int col = t; col < D; col += 256) {
+    int32_t s = 0;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) s += part[r][col];
+    store_digits(qdig + (bh * nQB + i) * 2 * D, D, col, s);
+  }
+}
+
+// One workgroup per (key block, head, batch).  Sums are kept per 32-row chunk
+// so that 2x32 groups, and groups that span two K scale blocks, combine their
+// chunks with the right scale.
+template <int D, bool VI8, int MAXCH>
 __global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
-  constexpr int MAXR = 128;
-  __shared__ __attribute__((aligned(16))) int8_t ktile[MAXR * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[MAXR * D];   // bf16 bits, or int8 codes (low byte)
-  __shared__ int32_t ks[MAXR / 32][D];
-  __shared__ float vs[MAXR / 32][D];
+  // MAXCH: 32-row chunks per key block (kblock / 32)
+  constexpr int KDW = D / 4, KRG = 256 / KDW;   // K: dwords per row, row groups
+  constexpr int VDW = VI8 ? D / 4 : D / 2, VRG = 256 / VDW;
+  static_assert(32 % KRG == 0 && 32 % VRG == 0, "row groups must divide a chunk");
+  __shared__ int32_t kpart[KRG][MAXCH][D];
+  __shared__ float vpart[VRG][MAXCH][D];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int64_t bh = (int64_t)b * a.H + h;
-  const int kb = a.kblock, row0 = j * kb, nch = kb / 32;
+  const int kb = MAXCH * 32, row0 = j * kb, nch = MAXCH;
   const int nKS = a.Lkv / a.k_scale_rows;
-  // stage K rows
-  const int8_t* ksrc = a.k + (bh * a.Lkv + row0) * D;
-  for (int v = t; v < kb * D / 16; v += 256)
-    reinterpret_cast<uint4*>(ktile)[v] = reinterpret_cast<const uint4*>(ksrc)[v];
-  // stage V rows (64-row blocks remapped through v_block_src)
-  if (a.G > 0) {
-    constexpr int EPV = VI8 ? 16 : 8;  // elements per 16-byte load
-    for (int v = t; v < kb * D / EPV; v += 256) {
-      const int r = v / (D / EPV), cc = v % (D / EPV);
-      const int lr = row0 + r;
-      int pr = lr;
-      if (a.v_block_src) {
-        int pb = a.v_block_src[lr / 64];
-        pb = min(max(pb, 0), a.Lv / 64 - 1);
-        pr = pb * 64 + lr % 64;
-      }
-      if (VI8) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(a.v) + (bh * a.Lv + pr) * D + cc * 16);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  const int nvalid = min(kb, max(0, a.lkv_valid - row0));
+  // K: lane (dw, rg) sums rows rg, rg + KRG, ... of each chunk
+  {
+    constexpr int NR = 32 / KRG;
+    const int dw = t % KDW, rg = t / KDW;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.k + (bh * a.Lkv + row0) * D) + dw;
+    uint32_t w[MAXCH][NR];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) vtile[r * D + cc * 16 + e] = (uint16_t)((w[e / 4] >> (8 * (e % 4))) & 0xFF);
+    for (int c = 0; c < MAXCH; ++c)
+#pragma unroll
+      for (int k = 0; k < NR; ++k) w[c][k] = src[(c * 32 + rg + KRG * k) * KDW];
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c) {
+      I8Cols acc;
+#pragma unroll
+      for (int k = 0; k < NR; ++k) acc.add(w[c][k], c * 32 + rg + KRG * k < nvalid);
+      *reinterpret_cast<int4*>(&kpart[rg][c][dw * 4]) = acc.sums();
+    }
+  }
+  // V (centroids only): physical rows through v_block_src, one 64-row block at a time
+  if (a.G > 0) {
+    constexpr int NR = 32 / VRG;
+    const int dw = t % VDW, rg = t / VDW;
+    uint32_t w[MAXCH][NR];
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c) {
+      int prow = row0 + c * 32;   // physical first row of the chunk
+      if (a.v_block_src) {
+        const int pb = min(max(a.v_block_src[(row0 + c * 32) / 64], 0), a.Lv / 64 - 1);
+        prow = pb * 64 + (row0 + c * 32) % 64;
+      }
+      const uint32_t* src =
+          VI8 ? reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(a.v) + (bh * a.Lv + prow) * D) + dw
+              : reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v) + (bh * a.Lv + prow) * D) + dw;
+#pragma unroll
+      for (int k = 0; k < NR; ++k) w[c][k] = src[(rg + VRG * k) * VDW];
+    }
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c) {
+      if (VI8) {
+        I8Cols acc;   // |sum| <= 127*32: exact in float
+#pragma unroll
+        for (int k = 0; k < NR; ++k) acc.add(w[c][k], c * 32 + rg + VRG * k < nvalid);
+        const int4 sm = acc.sums();
+        *reinterpret_cast<float4*>(&vpart[rg][c][dw * 4]) = make_float4((float)sm.x, (float)sm.y, (float)sm.z, (float)sm.w);
       } else {
-        reinterpret_cast<uint4*>(vtile)[(r * D + cc * 8) / 8] =
-            *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + (bh * a.Lv + pr) * D + cc * 8);
+        float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const bool valid = c * 32 + rg + VRG * k < nvalid;
+          acc0 += valid ? __uint_as_float(w[c][k] << 16) : 0.0f;
+          acc1 += valid ? __uint_as_float(w[c][k] & 0xFFFF0000u) : 0.0f;
+        }
+        *reinterpret_cast<float2*>(&vpart[rg][c][dw * 2]) = make_float2(acc0, acc1);
       }
     }
   }
   __syncthreads();
-  const int nvalid = min(kb, max(0, a.lkv_valid - row0));
+  // chunk sums into row 0 of the partial arrays (each element is read and
+  // written by the same thread only)
   for (int w = t; w < nch * D; w += 256) {
     const int c = w / D, col = w % D;
     int32_t s = 0;
-    float fv = 0.0f;
-    int32_t iv = 0;
-    for (int r = c * 32; r < c * 32 + 32 && r < nvalid; ++r) {
-      s += ktile[r * D + col];
-      if (a.G > 0) {
-        if (VI8) iv += (int32_t)(int8_t)(vtile[r * D + col] & 0xFF);
-        else fv += bf16_to_f32(vtile[r * D + col]);
-      }
+#pragma unroll
+    for (int r = 0; r < KRG; ++r) s += kpart[r][c][col];
+    float vsum = 0.0f;
+    if (a.G > 0) {
+#pragma unroll
+      for (int r = 0; r < VRG; ++r) vsum += vpart[r][c][col];
     }
-    ks[c][col] = s;
-    vs[c][col] = VI8 ? (float)iv : fv;   // |int sum| <= 127*32: exact in float
+    kpart[0][c][col] = s;
+    vpart[0][c][col] = vsum;
   }
   __syncthreads();
-  if (a.ksum) {
+  if (a.kdig) {
     for (int col = t; col < D; col += 256) {
       int32_t s = 0;
-      for (int c = 0; c < nch; ++c) s += ks[c][col];
-      a.ksum[((int64_t)bh * a.nKB + j) * D + col] = s;
+      for (int c = 0; c < nch; ++c) s += kpart[0][c][col];
+      store_digits(a.kdig + ((int64_t)bh * a.nKB + j) * 2 * D, D, col, s);
     }
   }
   if (a.G > 0) {
@@ -124,16 +192,16 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
       float ksum = 0.0f, vsum = 0.0f;
       for (int c = g * cpg; c < (g + 1) * cpg && c < nch; ++c) {
         const int crow = row0 + c * 32;
-        ksum += a.k_scale[bh * nKS + crow / a.k_scale_rows] * (float)ks[c][col];
+        ksum += a.k_scale[bh * nKS + crow / a.k_scale_rows] * (float)kpart[0][c][col];
         if (VI8) {
           int pr = crow;
           if (a.v_block_src) {
             int pb = min(max(a.v_block_src[crow / 64], 0), a.Lv / 64 - 1);
             pr = pb * 64 + crow % 64;
           }
-          vsum += a.v_scale[bh * (a.Lv / a.v_scale_rows) + pr / a.v_scale_rows] * vs[c][col];
+          vsum += a.v_scale[bh * (a.Lv / a.v_scale_rows) + pr / a.v_scale_rows] * vpart[0][c][col];
         } else {
-          vsum += vs[c][col];
+          vsum += vpart[0][c][col];
         }
       }
       const int64_t o = ((bh * a.nKB + j) * a.G + g);
@@ -144,87 +212,153 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
   }
 }
 
-// Sol decisions for QB query blocks of one (head, batch).  Dynamic LDS holds the
-// proxies s[QB][nKB] in float64.
-template <int D, int QB>
-__global__ __launch_bounds__(256) void decide_sol_kernel(RouteArgs a) {
-  extern __shared__ double sprox[];   // [QB][nKB]
-  __shared__ int32_t qs[QB][D];
-  __shared__ double red[4];
+// Sol decisions for 32 query blocks of one (head, batch), on the int8 matrix
+// cores.  The proxy numerator D_ij = Qsum_i . Ksum_j is exact: with
+// x = 128*hi + lo for both sums,
+//   D = 2^14 * sum(hq*hk) + 2^7 * sum(hq*lk + lq*hk) + sum(lq*lk),
+// three v_mfma_i32_32x32x32_i8 products (the middle one over 2d), each partial
+// sum below 2^22 in int32, combined exactly in float64.  s_ij = D * (b_j / n_j)
+// in float64.  Three passes over the key blocks recompute s (a 32x32 tile costs
+// 16 MFMAs): the mean, the population variance about it, then the decisions.
+// Each wave takes every NW-th 32-block column tile; lane (n, hf) holds
+// s[r][j] for rows r = (e/4)*8 + hf*4 + e%4 (e < 16) and column j = n.
+constexpr int kDecideWaves = 4;
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecideWaves) void decide_sol_kernel(RouteArgs a) {
+  constexpr int NS = D / 32;   // 32-channel MFMA k-steps
+  constexpr int NW = kDecideWaves;
+  __shared__ double red[NW][32];
+  __shared__ double colsum[NW][32][33];   // per wave: [row][column lane], padded
+  __shared__ double mu_s[32], thr_s[32];
+  __shared__ int keep_s[32];
   const int h = blockIdx.y, b = blockIdx.z, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = lane & 31, hf = lane >> 5;
   const int64_t bh = (int64_t)b * a.H + h;
-  const int i0 = blockIdx.x * QB, nq = min(QB, a.nQB - i0);
-  const int nKS = a.Lkv / a.k_scale_rows;
-  for (int w = t; w < QB * D; w += 256) {
-    const int qi = w / D, col = w % D;
-    qs[qi][col] = qi < nq ? a.qsum[(bh * a.nQB + i0 + qi) * D + col] : 0;
-  }
-  __syncthreads();
+  const int i0 = blockIdx.x * 32;
   const int kb = a.kblock;
-  auto is_cand = [&](int j) { return j * kb >= a.prefix && j * kb < a.lkv_valid; };
-  for (int j = t; j < a.nKB; j += 256) {
-    if (!is_cand(j)) continue;
-    double acc[QB];
-#pragma unroll
-    for (int qi = 0; qi < QB; ++qi) acc[qi] = 0.0;
-    const int32_t* kr = a.ksum + (bh * a.nKB + j) * D;
-#pragma unroll 2
-    for (int c8 = 0; c8 < D / 8; ++c8) {
-      const int4 k0 = reinterpret_cast<const int4*>(kr)[2 * c8];
-      const int4 k1 = reinterpret_cast<const int4*>(kr)[2 * c8 + 1];
-      const int kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-#pragma unroll
-      for (int qi = 0; qi < QB; ++qi) {
-        // |sum of 8 products| <= 8 * 16256^2 < 2^31: exact in int32
-        int32_t part = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part += __mul24(qs[qi][c8 * 8 + e], kk[e]);
-        acc[qi] += (double)part;
-      }
-    }
-    const double bj = (double)a.k_scale[bh * nKS + j];
-    const double nj = (double)min(kb, a.lkv_valid - j * kb);
-#pragma unroll
-    for (int qi = 0; qi < QB; ++qi) sprox[qi * a.nKB + j] = acc[qi] * bj / nj;
-  }
-  __syncthreads();
+  const int nKS = a.Lkv / a.k_scale_rows;
   // candidates form the contiguous range [jc0, jc1)
   const int jc0 = (a.prefix + kb - 1) / kb;
   const int jc1 = min(a.nKB, (a.lkv_valid + kb - 1) / kb);
   const int N = max(0, jc1 - jc0);
-  const double tau = (double)a.tau;
-  for (int qi = 0; qi < nq; ++qi) {
-    const int i = i0 + qi;
-    double s = 0.0;
-    for (int j = jc0 + t; j < jc1; j += 256) s += sprox[qi * a.nKB + j];
-    s = wave_sum_f64(s);
-    if (lane == 0) red[wave] = s;
-    __syncthreads();
-    const double mu = N > 0 ? (red[0] + red[1] + red[2] + red[3]) / N : __builtin_nan("");
-    __syncthreads();
-    double ss = 0.0;
-    for (int j = jc0 + t; j < jc1; j += 256) {
-      const double dlt = sprox[qi * a.nKB + j] - mu;
-      ss += dlt * dlt;
+  // A operands: digit rows of query block i0 + n (zero past the last block)
+  v4i qh[NS], ql[NS];
+  {
+    const bool ok = i0 + n < a.nQB;
+    const int8_t* qr = a.qdig + (bh * a.nQB + (ok ? i0 + n : 0)) * 2 * D + hf * 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qh[s] = ok ? *reinterpret_cast<const v4i*>(qr + s * 32) : (v4i){0, 0, 0, 0};
+      ql[s] = ok ? *reinterpret_cast<const v4i*>(qr + D + s * 32) : (v4i){0, 0, 0, 0};
     }
-    ss = wave_sum_f64(ss);
-    if (lane == 0) red[wave] = ss;
+  }
+  // key digits of column tile tt (lane: key block tt*32 + n, channels hf*16..)
+  struct KOps {
+    v4i h[NS], l[NS];
+  };
+  auto load_k = [&](int tt, KOps& k) __attribute__((always_inline)) {
+    const int j = tt * 32 + n;
+    const int8_t* kr = a.kdig + (bh * a.nKB + (j < a.nKB ? j : 0)) * 2 * D + hf * 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      k.h[s] = *reinterpret_cast<const v4i*>(kr + s * 32);
+      k.l[s] = *reinterpret_cast<const v4i*>(kr + D + s * 32);
+    }
+  };
+  // s for column tile tt (column n of this lane)
+  auto tile = [&](int tt, const KOps& k, double (&sv)[16]) __attribute__((always_inline)) {
+    const int j = tt * 32 + n;
+    v16i p1 = (v16i){}, p2 = (v16i){}, p3 = (v16i){};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      p1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qh[s], k.h[s], p1, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qh[s], k.l[s], p2, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ql[s], k.h[s], p2, 0, 0, 0);
+      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ql[s], k.l[s], p3, 0, 0, 0);
+    }
+    const double w = j < a.nKB ? (double)a.k_scale[bh * nKS + j] / (double)min(kb, a.lkv_valid - j * kb) : 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      sv[e] = (16384.0 * (double)p1[e] + 128.0 * (double)p2[e] + (double)p3[e]) * w;
+  };
+  const int t0 = jc0 / 32, t1 = (jc1 + 31) / 32;   // column tiles touching the candidates
+  // row r of lane element e
+  auto row_of = [&](int e) { return (e / 4) * 8 + hf * 4 + (e % 4); };
+  // per-row sum over the candidate columns of f(s, row), reduced over the workgroup into red[0][row]
+  auto row_sum = [&](auto f) __attribute__((always_inline)) {
+    double acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0;
+    KOps kn;
+    if (t0 + wave < t1) load_k(t0 + wave, kn);
+    for (int tt = t0 + wave; tt < t1; tt += NW) {
+      const KOps kc = kn;
+      if (tt + NW < t1) load_k(tt + NW, kn);   // next tile's operands in flight
+      double sv[16];
+      tile(tt, kc, sv);
+      const int j = tt * 32 + n;
+      const bool cand = j >= jc0 && j < jc1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += cand ? f(sv[e], row_of(e)) : 0.0;
+    }
+    // over the 32 columns held by lanes with the same hf: through LDS
+#pragma unroll
+    for (int e = 0; e < 16; ++e) colsum[wave][row_of(e)][n] = acc[e];
     __syncthreads();
-    const double sigma = N > 0 ? sqrt((red[0] + red[1] + red[2] + red[3]) / N) : __builtin_nan("");
+    if (lane < 32) {
+      double sum = 0.0;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) sum += colsum[wave][lane][c];
+      red[wave][lane] = sum;
+    }
     __syncthreads();
+    if (t < 32) {
+      double sum = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += red[w][t];
+      red[0][t] = sum;
+    }
+    __syncthreads();
+  };
+  row_sum([](double s, int) { return s; });
+  if (t < 32) mu_s[t] = N > 0 ? red[0][t] / N : __builtin_nan("");
+  __syncthreads();
+  row_sum([&](double s, int r) { const double dl = s - mu_s[r]; return dl * dl; });
+  const double tau = (double)a.tau;
+  if (t < 32) {
+    const double mu = mu_s[t];
+    const double sigma = N > 0 ? sqrt(red[0][t] / N) : __builtin_nan("");
     const bool keep_all = N == 0 || (tau > 0 && __builtin_isinf(tau)) || sigma == 0.0;
-    const double thr = keep_all ? 0.0 : mu + tau * sigma;
-    uint8_t* mrow = a.map + (bh * a.nQB + i) * a.nKB;
-    for (int j = t; j < a.nKB; j += 256) {
+    keep_s[t] = keep_all ? 1 : 0;
+    thr_s[t] = keep_all ? 0.0 : mu + tau * sigma;
+    if (a.stats && i0 + t < a.nQB) {
+      a.stats[(bh * a.nQB + i0 + t) * 2] = mu;
+      a.stats[(bh * a.nQB + i0 + t) * 2 + 1] = sigma;
+    }
+  }
+  __syncthreads();
+  // decisions for every key block: DROP past the valid keys, EXACT in the
+  // prefix, CENTROID for candidates above the threshold
+  const int nt = (a.nKB + 31) / 32;
+  for (int tt = wave; tt < nt; tt += NW) {
+    const int j = tt * 32 + n;
+    double sv[16];
+    const bool any_cand = tt * 32 + 31 >= jc0 && tt * 32 < jc1;
+    if (any_cand) {
+      KOps kc;
+      load_k(tt, kc);
+      tile(tt, kc, sv);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = row_of(e), i = i0 + r;
+      if (i >= a.nQB || j >= a.nKB) continue;
       uint8_t st;
       if (j * kb >= a.lkv_valid) st = 0;
       else if (j * kb < a.prefix) st = 1;
-      else st = (!keep_all && sprox[qi * a.nKB + j] > thr) ? 2 : 1;
-      mrow[j] = st;
-    }
-    if (a.stats && t == 0) {
-      a.stats[(bh * a.nQB + i) * 2] = mu;
-      a.stats[(bh * a.nQB + i) * 2 + 1] = sigma;
+      else st = (!keep_s[r] && sv[e] > thr_s[r]) ? 2 : 1;
+      a.map[(bh * a.nQB + i) * a.nKB + j] = st;
     }
   }
 }
@@ -250,36 +384,27 @@ __global__ __launch_bounds__(256) void decide_explicit_kernel(RouteArgs a) {
 
 size_t route_workspace_bytes(int B, int H, int nQB, int nKB, int d) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al((size_t)B * H * nQB * d * 4) + al((size_t)B * H * nKB * d * 4);
-}
-
-static int sol_qb(int nKB) {
-  // proxies of QB query blocks stay in LDS: QB * nKB * 8 bytes <= 64 KiB
-  int qb = 8;
-  while (qb > 1 && (size_t)qb * nKB * 8 > 65536) qb /= 2;
-  return qb;
+  return al((size_t)B * H * nQB * 2 * d) + al((size_t)B * H * nKB * 2 * d);
 }
 
 template <int D>
 static hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
   const bool sol = a.explicit_map == nullptr;
   if (sol) {
-    pool_q_kernel<D><<<dim3(a.nQB, a.H, a.B), 256, 0, st>>>(a.q, a.H, a.Lq, a.lq_valid, a.nQB, a.qsum);
+    pool_q_kernel<D><<<dim3(a.nQB, a.H, a.B), 256, 0, st>>>(a.q, a.H, a.Lq, a.lq_valid, a.nQB, a.qdig);
   }
   if (sol || a.G > 0) {
-    if (a.v_int8) pool_kv_kernel<D, true><<<dim3(a.nKB, a.H, a.B), 256, 0, st>>>(a);
-    else pool_kv_kernel<D, false><<<dim3(a.nKB, a.H, a.B), 256, 0, st>>>(a);
+    const dim3 grid(a.nKB, a.H, a.B);
+    if (a.kblock == 64) {
+      if (a.v_int8) pool_kv_kernel<D, true, 2><<<grid, 256, 0, st>>>(a);
+      else pool_kv_kernel<D, false, 2><<<grid, 256, 0, st>>>(a);
+    } else {
+      if (a.v_int8) pool_kv_kernel<D, true, 4><<<grid, 256, 0, st>>>(a);
+      else pool_kv_kernel<D, false, 4><<<grid, 256, 0, st>>>(a);
+    }
   }
   if (sol) {
-    const int qb = sol_qb(a.nKB);
-    const size_t lds = (size_t)qb * a.nKB * 8;
-    dim3 grid((a.nQB + qb - 1) / qb, a.H, a.B);
-    switch (qb) {
-      case 8: decide_sol_kernel<D, 8><<<grid, 256, lds, st>>>(a); break;
-      case 4: decide_sol_kernel<D, 4><<<grid, 256, lds, st>>>(a); break;
-      case 2: decide_sol_kernel<D, 2><<<grid, 256, lds, st>>>(a); break;
-      default: decide_sol_kernel<D, 1><<<grid, 256, lds, st>>>(a); break;
-    }
+    decide_sol_kernel<D><<<dim3((a.nQB + 31) / 32, a.H, a.B), 64 * kDecideWaves, 0, st>>>(a);
   } else {
     decide_explicit_kernel<<<dim3(a.nQB, a.H, a.B), 256, 0, st>>>(a);
   }

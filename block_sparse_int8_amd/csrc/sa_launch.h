@@ -50,8 +50,8 @@ struct RouteArgs {
   float* vc;
   float* cnt;
   double* stats;
-  int32_t* qsum;   // workspace [B,H,nQB,d] (Sol rule only)
-  int32_t* ksum;   // workspace [B,H,nKB,d] (Sol rule only)
+  int8_t* qdig;    // workspace [B,H,nQB][2][d]: query-block column sums as two int8 digits (Sol rule only)
+  int8_t* kdig;    // workspace [B,H,nKB][2][d]: key-block column sums, same form (Sol rule only)
 };
 
 struct FwdArgs {
@@ -79,7 +79,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 
-// Route workspace layout: qsum then ksum, each 256-byte aligned.
+// Route workspace layout: qdig then kdig, each 256-byte aligned.
 size_t route_workspace_bytes(int B, int H, int nQB, int nKB, int d);
 
 }  // namespace sa

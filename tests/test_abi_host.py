@@ -124,7 +124,7 @@ def test_route_validation(dims_kw, prm_kw, code, msg):
 def test_route_needs_workspace_for_sol_rule():
     dims, prm = _dims(), _prm()
     need = _lib().sparse_attn_route_workspace_size(ctypes.byref(dims), ctypes.byref(prm), 0)
-    assert need == 2 * 128 * 4 + 4 * 128 * 4   # qsum [1,1,2,128] + ksum [1,1,4,128] int32
+    assert need == 2 * 2 * 128 + 4 * 2 * 128   # query and key column sums, two int8 digit planes each
     assert _route(dims, prm) == sa.SA_E_WORKSPACE
     assert _route(dims, prm, ws=ctypes.c_void_p(256), wsb=need - 1) == sa.SA_E_WORKSPACE
     assert _route(dims, prm, ws=ctypes.c_void_p(260), wsb=need) == sa.SA_E_ALIGN
