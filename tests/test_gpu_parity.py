@@ -199,3 +199,38 @@ def test_centroid_only_row(sa, orc):
     """tau = -inf: every block a centroid; the output is a count-weighted
     softmax over centroids only."""
     _check_workload(orc, W.config(4, small=True), tau=float("-inf"))
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_sol_kblock128(sa, orc, G):
+    """Sol routing on 128-key blocks (one K scale per block): four 32-row chunks
+    per block sum, and centroid groups of 128 or 2 x 64 rows."""
+    wl = W.tiny_sol(seed=21, H=2, L=1024, d=128, valid=1000, centroids_per_block=G)
+    wl.kblock = 128
+    wl.k_scale_rows = 128
+    _check_workload(orc, wl, tau=0.5)
+
+
+def test_saturated_block_sums(sa, orc):
+    """Blocks whose codes are all +-127 with one sign per column: query block sums
+    and 128-key block sums reach +-127*128, the ends of the range the routing
+    proxy's two-digit split must cover; the other blocks stay random so the
+    proxy's spread is not degenerate."""
+    wl = W.tiny_sol(seed=22, H=2, L=1024, d=128, centroids_per_block=1)
+    wl.kblock = 128
+    wl.k_scale_rows = 128
+    rng = np.random.default_rng(23)
+    q = np.ascontiguousarray(wl.q.copy())
+    k = np.ascontiguousarray(wl.k.copy())
+    one, minus_one = bf16_bits(np.float32(1.0)), bf16_bits(np.float32(-1.0))
+    for h in range(wl.H):
+        for blk in (0, 3, 6):
+            signs = rng.integers(0, 2, size=wl.d).astype(bool)
+            q[0, h, blk * 128:(blk + 1) * 128, :] = np.where(signs, one, minus_one)
+            signs = rng.integers(0, 2, size=wl.d).astype(bool)
+            k[0, h, blk * 128:(blk + 1) * 128, :] = np.where(signs, one, minus_one)
+    wl.q, wl.k = q, k
+    g, o = _check_workload(orc, wl, tau=0.5)
+    # the saturated blocks really are at the extreme
+    assert np.abs(o["q8"][0, 0, :128].astype(np.int32).sum(axis=0)).max() == 127 * 128
+    assert np.abs(o["k8"][0, 0, 384:512].astype(np.int32).sum(axis=0)).max() == 127 * 128
