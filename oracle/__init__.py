@@ -62,11 +62,14 @@ def quantize(x_bits: np.ndarray, valid_len: Optional[int] = None, rows_per_block
 
 def route(q8, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, *, v_bits=None, v8=None, v_scale=None,
           v_scale_rows=128, v_block_src=None, tau=1.0, G=1, prefix=0, kblock=64,
-          explicit_map=None, map_kblock=None):
+          explicit_map=None, map_kblock=None, rule=0, sparsity=0.0):
     """Block map, centroids and routing statistics for one attention call.
+    ``rule`` 0 is the threshold rule (``tau``), 1 the fixed-sparsity rule
+    (``sparsity``, taken at float32 precision as the library's parameter is).
     Returns a dict with map uint8 [B,H,nQB,nKB], kbar/vbar float64
     [B,H,nKB,G,d], count float64 [B,H,nKB,G], stats float64 [B,H,nQB,2]
-    (mu, sigma; NaN for explicit maps) and tie uint8 [B,H,nQB,nKB]."""
+    (mu, sigma; NaN for explicit maps and the fixed-sparsity rule) and tie
+    uint8 [B,H,nQB,nKB]."""
     q8 = np.ascontiguousarray(q8, dtype=np.int8)
     k8 = np.ascontiguousarray(k8, dtype=np.int8)
     B, H, Lq, d = q8.shape
@@ -97,7 +100,8 @@ def route(q8, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, *, v_bits=None, v8
         if em.shape != (B, H, nQB, -(-Lkv // map_kblock)):
             raise ValueError(f"explicit map shape {em.shape}")
     rc = _lib().orc_route(_p(q8), _p(k8), _p(ks), k_scale_rows, _p(vb), _p(vi), _p(vsc), v_scale_rows,
-                          _p(vbs), Lv, B, H, Lq, Lkv, d, lq_valid, lkv_valid, ctypes.c_double(tau), G,
+                          _p(vbs), Lv, B, H, Lq, Lkv, d, lq_valid, lkv_valid, int(rule), ctypes.c_double(tau),
+                          ctypes.c_double(float(np.float32(sparsity))), G,
                           prefix, kblock, _p(em), map_kblock or kblock, _p(out_map), _p(kbar), _p(vbar),
                           _p(count), _p(stats), _p(tie))
     if rc != 0:
@@ -198,7 +202,8 @@ def run(wl, sel=None, tau=None):
         vkw = dict(v_bits=wl.v)
     r = route(q8, k8, ks, wl.k_scale_rows, wl.lq_valid, wl.lkv_valid, v_block_src=vbs, tau=tau,
               G=wl.centroids_per_block, prefix=wl.prefix_tokens, kblock=wl.kblock,
-              explicit_map=wl.explicit_map, map_kblock=wl.map_kblock, **vkw)
+              explicit_map=wl.explicit_map, map_kblock=wl.map_kblock, rule=wl.rule, sparsity=wl.sparsity,
+              **vkw)
     out, lse, sel = forward(q8, qs, k8, ks, wl.k_scale_rows, wl.lq_valid, wl.lkv_valid, r["map"],
                             kbar=r["kbar"], vbar=r["vbar"], count=r["count"], v_block_src=vbs,
                             kblock=wl.kblock, G=wl.centroids_per_block, sm_scale=wl.sm_scale, sel=sel, **vkw)

@@ -149,6 +149,15 @@ static double v_at(const orc_vsrc* s, int b, int h, int r, int c) {
 /* tau = +inf, sigma = 0 or no candidates: every candidate exact.            */
 /* tie[i,j] = 1 when |s_ij - (mu + tau*sigma)| <= 1e-6 * sigma.              */
 /*                                                                            */
+/* Fixed-sparsity rule (rule = 1; Ref2VA VSA, two-stage attention patch:     */
+/* top-k pruning of the video key tiles only, at a set sparsity such as      */
+/* 0.75, with 0.50-0.70 suggested as a start): of the N candidates of a query */
+/* block, floor(sparsity * N) are pruned (the product taken in float64) and  */
+/* the other N - floor(sparsity * N) stay exact: those with the largest      */
+/* s_ij, equal values ordered by lower key-block index first.  Pruned blocks */
+/* become centroids when centroids are kept (G > 0) and are dropped when     */
+/* G = 0.  Prefix blocks stay exact, empty blocks dropped; stats are NaN.    */
+/*                                                                            */
 /* Explicit maps (FlashVSR Sparge Attention, "How it works"): a map on       */
 /* logical blocks of map_kblock keys; physical block j takes the state of    */
 /* logical block j*kblock/map_kblock.  Values above 2 count as exact, and so */
@@ -162,14 +171,30 @@ static double v_at(const orc_vsrc* s, int b, int h, int r, int c) {
 /*                                                                            */
 /* Pinned by: brute force on tiny inputs, closed-form outlier example,       */
 /* tau = +/-inf cases, nesting in tau, scale invariance, 1x64 map == 2x32    */
-/* map, LCSA block count.  The proxy itself: parity unpinned (the pages do    */
-/* not define it).                                                            */
+/* map, LCSA block count; for the fixed-sparsity rule a hand-ordered        */
+/* example, brute force, equal-score ordering, kept counts and nesting in    */
+/* the sparsity.  The proxy itself: parity unpinned (the pages do not        */
+/* define it).                                                                */
 /* Returns 0, or -1 on bad arguments.                                         */
 /* ------------------------------------------------------------------------- */
+typedef struct {
+  double s;
+  int j;
+} orc_scored;
+
+/* Larger score first; equal scores by lower block index. */
+static int orc_rank_cmp(const void* pa, const void* pb) {
+  const orc_scored* a = (const orc_scored*)pa;
+  const orc_scored* b = (const orc_scored*)pb;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->j > b->j) - (a->j < b->j);
+}
+
 int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scale_rows,
               const uint16_t* v_bf16, const int8_t* v_i8, const float* v_scale, int v_scale_rows,
               const int32_t* v_block_src, int Lv, int B, int H, int Lq, int Lkv, int d, int lq_valid,
-              int lkv_valid, double tau, int G, int prefix, int kblock,
+              int lkv_valid, int rule, double tau, double sparsity, int G, int prefix, int kblock,
               const uint8_t* explicit_map, int map_kblock, uint8_t* map, double* kbar,
               double* vbar, double* count, double* stats, uint8_t* tie) {
   int nQB = (Lq + QBLOCK - 1) / QBLOCK;
@@ -177,7 +202,10 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
   int nKS = (Lkv + k_scale_rows - 1) / k_scale_rows;
   int nMB = explicit_map ? (Lkv + map_kblock - 1) / map_kblock : 0;
   if (G < 0 || G > 2 || (G > 0 && kblock % G)) return -1;
-  if (!explicit_map && (k_scale_rows != kblock || G == 0 || isnan(tau))) return -1;
+  if (!explicit_map && k_scale_rows != kblock) return -1;
+  if (!explicit_map && rule == 0 && (G == 0 || isnan(tau))) return -1;
+  if (!explicit_map && rule == 1 && !(sparsity >= 0.0 && sparsity <= 1.0)) return -1;
+  if (!explicit_map && rule != 0 && rule != 1) return -1;
   orc_vsrc vs = {v_bf16, v_i8, v_scale, v_scale_rows, v_block_src, Lv, H, d};
   int ok = 0;
 
@@ -191,6 +219,7 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
       int64_t* Ks = (int64_t*)calloc((size_t)nKB * d, sizeof(int64_t));
       int* nk = (int*)calloc((size_t)nKB, sizeof(int));
       double* s = (double*)malloc(sizeof(double) * (size_t)nKB);
+      orc_scored* ranked = (orc_scored*)malloc(sizeof(orc_scored) * (size_t)nKB);
       for (int i = 0; i < nQB; ++i)
         for (int t = i * QBLOCK; t < (i + 1) * QBLOCK && t < Lq && t < lq_valid; ++t)
           for (int c = 0; c < d; ++c) Qs[(int64_t)i * d + c] += qh[(int64_t)t * d + c];
@@ -254,6 +283,24 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
             s[j] = (double)D * (double)k_scale[bh * nKS + j] / (double)nk[j];
             ++N;
           }
+          if (rule == 1) {
+            /* fixed sparsity: keep the N - floor(sparsity * N) best-scored */
+            int n = 0;
+            for (int j = 0; j < nKB; ++j)
+              if (nk[j] > 0 && j * kblock >= prefix) {
+                ranked[n].s = s[j];
+                ranked[n].j = j;
+                ++n;
+              }
+            qsort(ranked, (size_t)n, sizeof(orc_scored), orc_rank_cmp);
+            int keep = N - (int)floor(sparsity * (double)N);
+            for (int r = 0; r < n; ++r) mrow[ranked[r].j] = r < keep ? ORC_EXACT : (G > 0 ? ORC_CENTROID : ORC_DROP);
+            if (stats) {
+              stats[(bh * nQB + i) * 2] = NAN;
+              stats[(bh * nQB + i) * 2 + 1] = NAN;
+            }
+            continue;
+          }
           if (N > 0) {
             double sum = 0.0;
             for (int j = 0; j < nKB; ++j)
@@ -281,6 +328,7 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
       free(Ks);
       free(nk);
       free(s);
+      free(ranked);
     }
   return ok;
 }

@@ -198,3 +198,148 @@ def test_empty_key_blocks_drop_and_ragged(orc):
     m = _route(orc, wl, q8, k8, ks)["map"]
     assert (m[..., 5:] == DROP).all()      # key rows >= 320 are all padding
     assert (m[..., :5] != DROP).all()
+
+
+# ---------------------------------------------------------------------------
+# Fixed-sparsity rule (Ref2VA VSA, two-stage attention patch: top-k pruning of
+# the generated-video key tiles only, at a set sparsity such as 0.75).
+# ---------------------------------------------------------------------------
+
+def _ordered_case():
+    """One query block whose rows are all e0 and seven key blocks: block j has
+    k[0] = c_j on every row (block 6 is padding).  Each proxy is then a positive
+    multiple of c_j, so the ranking is the ranking of c."""
+    d = 64
+    c = [3.0, -1.0, 5.0, 2.0, 4.0, 0.5]
+    q = np.zeros((1, 1, 128, d), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, 448, d), np.float32)
+    for j, cj in enumerate(c):
+        k[0, 0, j * 64:(j + 1) * 64, 0] = cj
+    v = np.zeros((1, 1, 448, d), np.float32)
+    return bf16_bits(q), bf16_bits(k), bf16_bits(v)
+
+
+@pytest.mark.parametrize("sparsity,G,prefix,expect", [
+    # ranking by c: blocks 2, 4, 0, 3, 5, 1
+    (0.5, 1, 0, [EXACT, CENTROID, EXACT, CENTROID, EXACT, CENTROID]),     # prune floor(3.0) = 3
+    (0.7, 1, 0, [CENTROID, CENTROID, EXACT, CENTROID, EXACT, CENTROID]),  # prune floor(4.2) = 4
+    (0.3, 1, 0, [EXACT, CENTROID, EXACT, EXACT, EXACT, EXACT]),           # prune floor(1.8) = 1
+    (0.0, 1, 0, [EXACT] * 6),
+    (1.0, 2, 0, [CENTROID] * 6),
+    (0.5, 0, 0, [EXACT, DROP, EXACT, DROP, EXACT, DROP]),                 # no centroids: pruned blocks drop
+    (0.5, 1, 64, [EXACT, CENTROID, EXACT, EXACT, EXACT, CENTROID]),       # block 0 exempt; 5 candidates, prune 2
+])
+def test_topk_hand_ordered(orc, sparsity, G, prefix, expect):
+    qb, kb, vb = _ordered_case()
+    q8, qs = orc.quantize(qb, rows_per_block=128)
+    k8, ks = orc.quantize(kb, valid_len=384, rows_per_block=64)
+    r = orc.route(q8, k8, ks, 64, 128, 384, v_bits=vb, G=G, kblock=64, prefix=prefix, rule=1,
+                  sparsity=sparsity)
+    assert r["map"][0, 0, 0].tolist() == expect + [DROP]
+    assert np.isnan(r["stats"]).all()
+
+
+def test_topk_equal_scores_keep_lower_index(orc):
+    d = 64
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 2, 256, d)).astype(np.float32)
+    blk = rng.standard_normal((64, d)).astype(np.float32)
+    k = np.tile(blk, (10, 1))[None, None].repeat(2, axis=1)
+    v = rng.standard_normal((1, 2, 640, d)).astype(np.float32)
+    q8, qs = orc.quantize(bf16_bits(q), rows_per_block=128)
+    k8, ks = orc.quantize(bf16_bits(k), rows_per_block=64)
+    r = orc.route(q8, k8, ks, 64, 256, 640, v_bits=bf16_bits(v), G=1, kblock=64, rule=1, sparsity=0.75)
+    # 10 equal scores: prune floor(7.5) = 7, keep blocks 0..2
+    assert (r["map"][..., :3] == EXACT).all() and (r["map"][..., 3:] == CENTROID).all()
+
+
+def _brute_topk(q8, qs, k8, ks, lq_valid, lkv_valid, sparsity, prefix=0, kblock=64):
+    """Independent float64 formulation: proxy = dot of the dequantized block
+    means over sqrt(d); keep the N - floor(sparsity*N) largest (stable order).
+    Returns (map, rows whose kept/pruned boundary is too close to call)."""
+    B, H, Lq, d = q8.shape
+    Lkv = k8.shape[2]
+    nQB, nKB = Lq // 128, Lkv // kblock
+    out = np.zeros((B, H, nQB, nKB), np.uint8)
+    close = np.zeros((B, H, nQB), bool)
+    sp = float(np.float32(sparsity))
+    for b in range(B):
+        for h in range(H):
+            qd = q8[b, h].astype(np.float64) * np.repeat(qs[b, h].astype(np.float64), 128)[:, None]
+            kd = k8[b, h].astype(np.float64) * np.repeat(ks[b, h].astype(np.float64), kblock)[:, None]
+            km = [kd[j * kblock:min((j + 1) * kblock, lkv_valid)].mean(0) if j * kblock < lkv_valid else None
+                  for j in range(nKB)]
+            cand = [j for j in range(nKB) if km[j] is not None and j * kblock >= prefix]
+            for i in range(nQB):
+                for j in range(nKB):
+                    out[b, h, i, j] = EXACT if km[j] is not None else DROP
+                if i * 128 >= lq_valid or not cand:
+                    continue
+                qm = qd[i * 128:min((i + 1) * 128, lq_valid)].mean(0)
+                s = np.array([qm @ km[j] / math.sqrt(d) for j in cand])
+                keep = len(cand) - int(math.floor(sp * len(cand)))
+                order = np.argsort(-s, kind="stable")
+                for r, jj in enumerate(order):
+                    if r >= keep:
+                        out[b, h, i, cand[jj]] = CENTROID
+                if 0 < keep < len(cand):
+                    a, c = s[order[keep - 1]], s[order[keep]]
+                    close[b, h, i] = abs(a - c) <= 1e-9 * max(abs(a), abs(c), 1e-300)
+    return out, close
+
+
+@pytest.mark.parametrize("sparsity", [0.5, 0.75, 0.6])
+def test_topk_matches_float64_brute_force(orc, sparsity):
+    wl = W.tiny_sol(seed=12, H=3, L=768, d=64, valid=700)
+    q8, qs, k8, ks = _quantized(orc, wl)
+    r = _route(orc, wl, q8, k8, ks, rule=1, sparsity=sparsity)
+    ref, close = _brute_topk(q8, qs, k8, ks, wl.lq_valid, wl.lkv_valid, sparsity)
+    assert not close.all()
+    rows = ~close
+    assert np.array_equal(r["map"][rows], ref[rows])
+
+
+def test_topk_prefix_brute_force(orc):
+    wl = W.config(4, small=True)
+    q8, qs, k8, ks = _quantized(orc, wl)
+    r = _route(orc, wl, q8, k8, ks, rule=1, sparsity=0.75)
+    ref, close = _brute_topk(q8, qs, k8, ks, wl.lq_valid, wl.lkv_valid, 0.75, prefix=wl.prefix_tokens)
+    assert np.array_equal(r["map"][~close], ref[~close])
+    npre = wl.prefix_tokens // 64
+    assert (r["map"][..., :npre] == EXACT).all()
+
+
+def test_topk_counts_and_nesting(orc):
+    wl = W.config(3, small=True)
+    q8, qs, k8, ks = _quantized(orc, wl)
+    nvalid = -(-wl.lkv_valid // 64)
+    prev = None
+    for sp in [0.0, 0.25, 0.5, 0.7, 0.75, 0.9, 1.0]:
+        m = _route(orc, wl, q8, k8, ks, rule=1, sparsity=sp)["map"]
+        kept = (m[..., :nvalid] == EXACT).sum(axis=-1)
+        assert (kept == nvalid - math.floor(float(np.float32(sp)) * nvalid)).all()
+        assert (m[..., nvalid:] == DROP).all()
+        ex = m == EXACT
+        if prev is not None:
+            assert not (ex & ~prev).any(), "raising the sparsity must only remove exact blocks"
+        prev = ex
+
+
+def test_topk_power_of_two_scaling_invariance(orc):
+    wl = W.config(3, small=True)
+    q8, qs, k8, ks = _quantized(orc, wl)
+    base = _route(orc, wl, q8, k8, ks, rule=1, sparsity=0.75)["map"]
+    wl2 = W.config(3, small=True)
+    wl2.q = bf16_bits(bf16_to_f32(wl.q) * 2.0)
+    wl2.k = bf16_bits(bf16_to_f32(wl.k) * 0.25)
+    q8b, qsb, k8b, ksb = _quantized(orc, wl2)
+    assert np.array_equal(_route(orc, wl2, q8b, k8b, ksb, rule=1, sparsity=0.75)["map"], base)
+
+
+def test_topk_rejects_bad_sparsity(orc):
+    wl = W.tiny_sol(seed=1, H=1, L=256, d=64)
+    q8, qs, k8, ks = _quantized(orc, wl)
+    for sp in (-0.1, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            _route(orc, wl, q8, k8, ks, rule=1, sparsity=sp)

@@ -62,6 +62,8 @@ class Workload:
     k: np.ndarray                      # bf16 bits [B,H,Lkv_phys,d] (physical K for virtual KV)
     v: np.ndarray                      # bf16 bits [B,H,Lv,d]
     threshold: float = 1.0
+    rule: int = 0                      # 0: threshold rule; 1: fixed sparsity (top-k of the candidates)
+    sparsity: float = 0.0              # fraction of candidates pruned under the fixed-sparsity rule
     centroids_per_block: int = 1
     prefix_tokens: int = 0
     kblock: int = 64
