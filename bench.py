@@ -2,7 +2,8 @@
 
 A step is the whole per-call path on one stream, inputs already resident in HBM:
 quantize_qk_int8(Q, 128-row blocks) -> quantize_qk_int8(K, 64-row blocks) ->
-sparse_attn_route (Sol 1x64, threshold 1.0) -> sparse_attn_fwd.
+sparse_attn_route (Sol 1x64, threshold 1.0; or the fixed-sparsity rule with
+--rule topk) -> sparse_attn_fwd.
 Workload: B=1, H=40, d=128, L=32768 (21 frames x 30x52 = 32760 valid tokens +
 8 padding rows), per-frame low-rank correlated bf16 Q/K/V (synthetic, seeded).
 
@@ -88,7 +89,8 @@ def cpu_baseline(wl, sample_stride: int):
     q8, qs = oracle.quantize(wl.q, wl.lq_valid, 128)
     k8, ks = oracle.quantize(wl.k, wl.lkv_valid, 64)
     t1 = time.perf_counter()
-    r = oracle.route(q8, k8, ks, 64, wl.lq_valid, wl.lkv_valid, v_bits=wl.v, tau=wl.threshold, G=1, kblock=64)
+    r = oracle.route(q8, k8, ks, 64, wl.lq_valid, wl.lkv_valid, v_bits=wl.v, tau=wl.threshold, G=1, kblock=64,
+                     rule=wl.rule, sparsity=wl.sparsity)
     t2 = time.perf_counter()
     nQB = wl.Lq // 128
     total = wl.B * wl.H * nQB
@@ -111,6 +113,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-stride", type=int, default=80)
     ap.add_argument("--heads", type=int, default=40, help="heads (40 for the measured workload)")
+    ap.add_argument("--rule", choices=["threshold", "topk"], default="threshold",
+                    help="routing rule: Sol threshold 1.0 (the measured workload) or fixed sparsity")
+    ap.add_argument("--sparsity", type=float, default=0.75, help="pruned fraction for --rule topk")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scales HBM counters under rocprofv3)")
     args = ap.parse_args()
@@ -126,6 +131,9 @@ def main():
     sa.device_check(0)
     t = time.perf_counter()
     wl = W.wan_like(H=args.heads)
+    topk = args.rule == "topk"
+    if topk:
+        wl.rule, wl.sparsity = 1, args.sparsity
     log(f"[bench] generated {wl.name}: B={wl.B} H={wl.H} L={wl.Lq} d={wl.d} in {time.perf_counter() - t:.1f}s")
     q, k, v = bf16_dev(wl.q), bf16_dev(wl.k), bf16_dev(wl.v)
     B, H, L, d = q.shape
@@ -153,7 +161,7 @@ def main():
         if ev: ev[2].record(stream)
         r = sa.sparse_attn_route(q8, k8, ks, v, lq_valid=wl.lq_valid, lkv_valid=wl.lkv_valid,
                                  threshold=wl.threshold, centroids_per_block=1, kblock=64, workspace=ws,
-                                 outputs=routed)
+                                 rule=wl.rule, sparsity=wl.sparsity, outputs=routed)
         ws = r["workspace"]
         if ev: ev[3].record(stream)
         sa.sparse_attn_fwd(q8, qs, k8, ks, v, routed["map"], k_centroid=routed["k_centroid"],
@@ -202,8 +210,9 @@ def main():
     value = dense_ops / (ms_step * 1e-3) / 1e12
     valid_blocks = -(-wl.lkv_valid // 64)
     kept = float((bmap[..., :valid_blocks] == 1).mean())
+    rule_desc = f"top-k sparsity {wl.sparsity:g}" if topk else f"threshold {wl.threshold:g}"
     res = {
-        "metric": METRIC,
+        "metric": METRIC if not topk else METRIC.replace("thr=1.0", f"top-k sparsity={wl.sparsity:g}"),
         "value": round(value, 3),
         "unit": "dense-equiv TOPS",
         "n_gpus": 1,
@@ -215,9 +224,10 @@ def main():
         "vs_baseline": None,
         "dtype": "int8 QK^T + fp32 softmax + bf16 PV",
         "data": "synthetic (seeded per-frame low-rank correlated bf16 Q/K/V)",
-        "config": {"workload": "Wan-14B-like Sol 1x64: B=1 H=40 d=128 L=32768 (32760 valid), threshold 1.0",
+        "config": {"workload": f"Wan-14B-like Sol 1x64: B=1 H={H} d=128 L=32768 (32760 valid), {rule_desc}",
                    "B": B, "H": H, "L": L, "d": d, "valid": wl.lkv_valid, "kblock": 64, "centroids": "1x64",
-                   "threshold": wl.threshold, "out_dtype": "bf16", "parallelism": "single GPU"},
+                   "rule": args.rule, "threshold": wl.threshold, "sparsity": wl.sparsity if topk else None,
+                   "out_dtype": "bf16", "parallelism": "single GPU"},
         "stages_ms": {"quantize_q": round(float(stage_ms[0]), 4), "quantize_k": round(float(stage_ms[1]), 4),
                       "route": round(float(stage_ms[2]), 4), "fwd": round(fwd_ms, 4)},
         "routing": {"kept_fraction": round(kept, 5), "exact_tiles": int(exact_tiles), "centroid_columns": int(cols),

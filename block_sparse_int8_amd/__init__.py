@@ -22,10 +22,11 @@ from typing import Optional, Sequence
 
 import torch
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 SA_OK, SA_E_NULL, SA_E_SHAPE, SA_E_ALIGN, SA_E_VALUE, SA_E_UNSUPPORTED, SA_E_DEVICE, SA_E_LAUNCH, SA_E_WORKSPACE = range(9)
 SA_DROP, SA_EXACT, SA_CENTROID = 0, 1, 2
 SA_BF16, SA_INT8, SA_F32 = 0, 1, 2
+SA_RULE_THRESHOLD, SA_RULE_TOPK = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -45,7 +46,7 @@ class sa_dims(ctypes.Structure):
 class sa_route_params(ctypes.Structure):
     _fields_ = [("threshold", ctypes.c_float)] + [
         (n, ctypes.c_int32) for n in ("centroids_per_block", "prefix_tokens", "kblock", "k_scale_rows",
-                                      "v_scale_rows", "map_kblock")]
+                                      "v_scale_rows", "map_kblock", "rule")] + [("sparsity", ctypes.c_float)]
 
 
 def search_paths():
@@ -156,8 +157,10 @@ def _dims(B, H, Lq, Lkv, d, lq_valid, lkv_valid, Lv):
     return sa_dims(B, H, Lq, Lkv, d, lq_valid, lkv_valid, Lv)
 
 
-def _params(threshold, G, prefix, kblock, k_scale_rows, v_scale_rows, map_kblock):
-    return sa_route_params(float(threshold), G, prefix, kblock, k_scale_rows, v_scale_rows, map_kblock)
+def _params(threshold, G, prefix, kblock, k_scale_rows, v_scale_rows, map_kblock, rule=SA_RULE_THRESHOLD,
+            sparsity=0.0):
+    return sa_route_params(float(threshold), G, prefix, kblock, k_scale_rows, v_scale_rows, map_kblock, int(rule),
+                           float(sparsity))
 
 
 def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor, v: torch.Tensor, *,
@@ -166,10 +169,12 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
                       threshold: float = 1.0, centroids_per_block: int = 1, prefix_tokens: int = 0,
                       kblock: int = 64, k_scale_rows: Optional[int] = None, v_scale_rows: int = 128,
                       explicit_map: Optional[torch.Tensor] = None, map_kblock: Optional[int] = None,
+                      rule: int = SA_RULE_THRESHOLD, sparsity: float = 0.0,
                       row_stats: bool = False, workspace: Optional[torch.Tensor] = None,
                       outputs: Optional[dict] = None, stream=None) -> dict:
-    """Block map + centroids.  Returns dict(map, k_centroid, v_centroid, count,
-    row_stats) with the shapes of sparse_attn.h."""
+    """Block map + centroids.  ``rule`` picks the threshold rule (``threshold``)
+    or the fixed-sparsity rule (``sparsity``).  Returns dict(map, k_centroid,
+    v_centroid, count, row_stats) with the shapes of sparse_attn.h."""
     B, H, Lq, d = q8.shape
     Lkv = k8.shape[2]
     Lv = v.shape[2]
@@ -191,7 +196,7 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
     if explicit_map is not None:
         _need(explicit_map, "explicit_map", torch.uint8, (B, H, nQB, Lkv // map_kblock))
     dims = _dims(B, H, Lq, Lkv, d, lq_valid, lkv_valid, Lv)
-    prm = _params(threshold, G, prefix_tokens, kblock, k_scale_rows, v_scale_rows, map_kblock)
+    prm = _params(threshold, G, prefix_tokens, kblock, k_scale_rows, v_scale_rows, map_kblock, rule, sparsity)
     lib = load()
     outputs = {} if outputs is None else outputs
     dev = q8.device
@@ -301,7 +306,7 @@ def gather_virtual_kv(k_phys: torch.Tensor, rows_per_slice: int, src_map: Sequen
 def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, lq_valid=None, lkv_valid=None,
                      threshold: float = 1.0, centroids_per_block: int = 1, prefix_tokens: int = 0,
                      explicit_map: Optional[torch.Tensor] = None, map_kblock: Optional[int] = None,
-                     kblock: int = 64, sm_scale: Optional[float] = None, out_dtype=torch.float32,
+                     rule: int = SA_RULE_THRESHOLD, sparsity: float = 0.0, kblock: int = 64, sm_scale: Optional[float] = None, out_dtype=torch.float32,
                      return_lse: bool = False, stream=None):
     """quantize_qk_int8(Q, 128 rows) -> quantize_qk_int8(K, kblock rows) ->
     sparse_attn_route -> sparse_attn_fwd, all on one stream.  q, k, v are bf16
@@ -313,7 +318,8 @@ def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, lq_va
     k8, ks = quantize_qk_int8(k, lkv_valid, kblock, stream=stream)
     r = sparse_attn_route(q8, k8, ks, v, lq_valid=lq_valid, lkv_valid=lkv_valid, threshold=threshold,
                           centroids_per_block=centroids_per_block, prefix_tokens=prefix_tokens, kblock=kblock,
-                          explicit_map=explicit_map, map_kblock=map_kblock, stream=stream)
+                          explicit_map=explicit_map, map_kblock=map_kblock, rule=rule, sparsity=sparsity,
+                          stream=stream)
     res = sparse_attn_fwd(q8, qs, k8, ks, v, r["map"], k_centroid=r["k_centroid"], v_centroid=r["v_centroid"],
                           count=r["count"], lq_valid=lq_valid, lkv_valid=lkv_valid,
                           centroids_per_block=centroids_per_block, kblock=kblock, sm_scale=sm_scale,

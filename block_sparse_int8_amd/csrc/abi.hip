@@ -165,12 +165,18 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
   const int G = p->centroids_per_block;
   const bool sol = explicit_map == nullptr;
   if (sol) {
-    if (G == 0) return fail(SA_E_VALUE, "sparse_attn_route: the Sol rule needs centroids_per_block 1 or 2");
-    if (isnan(p->threshold)) return fail(SA_E_VALUE, "sparse_attn_route: threshold is NaN");
+    if (p->rule != SA_RULE_THRESHOLD && p->rule != SA_RULE_TOPK)
+      return fail(SA_E_VALUE, "sparse_attn_route: rule must be SA_RULE_THRESHOLD or SA_RULE_TOPK (got %d)", p->rule);
+    if (p->rule == SA_RULE_THRESHOLD) {
+      if (G == 0) return fail(SA_E_VALUE, "sparse_attn_route: the threshold rule needs centroids_per_block 1 or 2");
+      if (isnan(p->threshold)) return fail(SA_E_VALUE, "sparse_attn_route: threshold is NaN");
+    } else if (!(p->sparsity >= 0.0f && p->sparsity <= 1.0f)) {
+      return fail(SA_E_VALUE, "sparse_attn_route: sparsity must lie in [0, 1]");
+    }
     if (p->k_scale_rows != p->kblock)
-      return fail(SA_E_VALUE, "sparse_attn_route: the Sol rule needs one K scale per key block (k_scale_rows == kblock)");
+      return fail(SA_E_VALUE, "sparse_attn_route: routing rules need one K scale per key block (k_scale_rows == kblock)");
     if ((size_t)(dims->Lkv / p->kblock) * 8 > 49152)
-      return fail(SA_E_SHAPE, "sparse_attn_route: at most 6144 key blocks per row for the Sol rule");
+      return fail(SA_E_SHAPE, "sparse_attn_route: at most 6144 key blocks per row for the routing rules");
   } else {
     if (p->map_kblock < p->kblock || p->map_kblock % p->kblock || dims->Lkv % p->map_kblock)
       return fail(SA_E_VALUE, "sparse_attn_route: map_kblock (%d) must be a multiple of kblock dividing Lkv", p->map_kblock);
@@ -198,6 +204,7 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
   a.nQB = dims->Lq / 128; a.nKB = dims->Lkv / p->kblock; a.kblock = p->kblock; a.G = G;
   a.prefix = p->prefix_tokens; a.k_scale_rows = p->k_scale_rows; a.v_scale_rows = p->v_scale_rows;
   a.map_kblock = sol ? p->kblock : p->map_kblock; a.tau = p->threshold;
+  a.rule = p->rule == SA_RULE_TOPK ? sa::kRuleTopK : sa::kRuleThreshold; a.sparsity = p->sparsity;
   a.explicit_map = explicit_map; a.map = block_map; a.kc = k_centroid; a.vc = v_centroid; a.cnt = count;
   a.stats = row_stats;
   if (sol) {

@@ -13,9 +13,10 @@
 //   pool_kv  — int32 column sums of each key block (into the workspace, for the
 //              proxy) and per-group centroids: kbar = mean of the dequantized
 //              keys, vbar = mean of V, count = valid rows
-//   decide   — proxy s_ij = (Qsum_i . Ksum_j) * b_j / n_j (exact integer dot in
-//              int32 pieces of 8 products, accumulated in float64), mean and
-//              population std over the candidates in float64, decisions; or the
+//   decide   — proxy s_ij = (Qsum_i . Ksum_j) * b_j / n_j (exact integer dot on
+//              the int8 matrix cores, combined in float64), then the threshold
+//              rule (mean and population std over the candidates in float64),
+//              the fixed-sparsity rule (top-k by exact radix select), or the
 //              explicit-map expansion.
 #include "sa_device.h"
 #include "sa_launch.h"
@@ -212,39 +213,29 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
   }
 }
 
-// Sol decisions for 32 query blocks of one (head, batch), on the int8 matrix
-// cores.  The proxy numerator D_ij = Qsum_i . Ksum_j is exact: with
-// x = 128*hi + lo for both sums,
+// Proxies for 32 query blocks of one (head, batch) against 32-block column
+// tiles of key blocks, on the int8 matrix cores.  The proxy numerator
+// D_ij = Qsum_i . Ksum_j is exact: with x = 128*hi + lo for both sums,
 //   D = 2^14 * sum(hq*hk) + 2^7 * sum(hq*lk + lq*hk) + sum(lq*lk),
 // three v_mfma_i32_32x32x32_i8 products (the middle one over 2d), each partial
 // sum below 2^22 in int32, combined exactly in float64.  s_ij = D * (b_j / n_j)
-// in float64.  Three passes over the key blocks recompute s (a 32x32 tile costs
-// 16 MFMAs): the mean, the population variance about it, then the decisions.
-// Each wave takes every NW-th 32-block column tile; lane (n, hf) holds
-// s[r][j] for rows r = (e/4)*8 + hf*4 + e%4 (e < 16) and column j = n.
-constexpr int kDecideWaves = 4;
-
+// in float64.  A 32x32 tile costs 16 MFMAs, so the decision kernels recompute
+// s on every pass over the key blocks instead of storing it.
+//
+// Lane (n, hf) of a tile holds s[r][j] for rows r = (e/4)*8 + hf*4 + e%4
+// (e < 16) and column j = n.
 template <int D>
-__global__ __launch_bounds__(64 * kDecideWaves) void decide_sol_kernel(RouteArgs a) {
-  constexpr int NS = D / 32;   // 32-channel MFMA k-steps
-  constexpr int NW = kDecideWaves;
-  __shared__ double red[NW][32];
-  __shared__ double colsum[NW][32][33];   // per wave: [row][column lane], padded
-  __shared__ double mu_s[32], thr_s[32];
-  __shared__ int keep_s[32];
-  const int h = blockIdx.y, b = blockIdx.z, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int n = lane & 31, hf = lane >> 5;
-  const int64_t bh = (int64_t)b * a.H + h;
-  const int i0 = blockIdx.x * 32;
-  const int kb = a.kblock;
-  const int nKS = a.Lkv / a.k_scale_rows;
-  // candidates form the contiguous range [jc0, jc1)
-  const int jc0 = (a.prefix + kb - 1) / kb;
-  const int jc1 = min(a.nKB, (a.lkv_valid + kb - 1) / kb);
-  const int N = max(0, jc1 - jc0);
-  // A operands: digit rows of query block i0 + n (zero past the last block)
-  v4i qh[NS], ql[NS];
-  {
+struct ProxyTiles {
+  static constexpr int NS = D / 32;   // 32-channel MFMA k-steps
+  struct KOps {
+    v4i h[NS], l[NS];
+  };
+  v4i qh[NS], ql[NS];   // A operands: digit rows of query block i0 + n (zero past the last block)
+  int64_t bh;
+  int n, hf, kb, nKS;
+
+  __device__ __forceinline__ ProxyTiles(const RouteArgs& a, int64_t bh_, int i0, int lane)
+      : bh(bh_), n(lane & 31), hf(lane >> 5), kb(a.kblock), nKS(a.Lkv / a.k_scale_rows) {
     const bool ok = i0 + n < a.nQB;
     const int8_t* qr = a.qdig + (bh * a.nQB + (ok ? i0 + n : 0)) * 2 * D + hf * 16;
 #pragma unroll
@@ -254,10 +245,7 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_sol_kernel(RouteArgs
     }
   }
   // key digits of column tile tt (lane: key block tt*32 + n, channels hf*16..)
-  struct KOps {
-    v4i h[NS], l[NS];
-  };
-  auto load_k = [&](int tt, KOps& k) __attribute__((always_inline)) {
+  __device__ __forceinline__ void load_k(const RouteArgs& a, int tt, KOps& k) const {
     const int j = tt * 32 + n;
     const int8_t* kr = a.kdig + (bh * a.nKB + (j < a.nKB ? j : 0)) * 2 * D + hf * 16;
 #pragma unroll
@@ -265,9 +253,9 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_sol_kernel(RouteArgs
       k.h[s] = *reinterpret_cast<const v4i*>(kr + s * 32);
       k.l[s] = *reinterpret_cast<const v4i*>(kr + D + s * 32);
     }
-  };
+  }
   // s for column tile tt (column n of this lane)
-  auto tile = [&](int tt, const KOps& k, double (&sv)[16]) __attribute__((always_inline)) {
+  __device__ __forceinline__ void tile(const RouteArgs& a, int tt, const KOps& k, double (&sv)[16]) const {
     const int j = tt * 32 + n;
     v16i p1 = (v16i){}, p2 = (v16i){}, p3 = (v16i){};
 #pragma unroll
@@ -281,30 +269,80 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_sol_kernel(RouteArgs
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       sv[e] = (16384.0 * (double)p1[e] + 128.0 * (double)p2[e] + (double)p3[e]) * w;
-  };
-  const int t0 = jc0 / 32, t1 = (jc1 + 31) / 32;   // column tiles touching the candidates
-  // row r of lane element e
-  auto row_of = [&](int e) { return (e / 4) * 8 + hf * 4 + (e % 4); };
+  }
+  __device__ __forceinline__ int row_of(int e) const { return (e / 4) * 8 + hf * 4 + (e % 4); }
+};
+
+// Work item of a decision workgroup: (32-query-block chunk, head, batch) from a
+// 1-D grid of chunks * H * B.  Hardware workgroup id w runs on XCD w % 8; each
+// XCD is given a contiguous range of work items, so the chunks of one head,
+// which all read that head's key-block sums, share one L2.
+struct DecideItem {
+  int i0, h, b;
+  __device__ __forceinline__ DecideItem(const RouteArgs& a) {
+    const int nwg = gridDim.x, nch = (a.nQB + 31) / 32;
+    int w = blockIdx.x;
+    if ((nwg & 7) == 0) w = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    i0 = (w % nch) * 32;
+    h = (w / nch) % a.H;
+    b = w / (nch * a.H);
+  }
+};
+
+// Routing candidates form the contiguous key-block range [jc0, jc1): blocks
+// with a valid row at or after the protected prefix.
+struct CandRange {
+  int jc0, jc1, N;
+  __device__ __forceinline__ explicit CandRange(const RouteArgs& a) {
+    jc0 = (a.prefix + a.kblock - 1) / a.kblock;
+    jc1 = min(a.nKB, (a.lkv_valid + a.kblock - 1) / a.kblock);
+    N = max(0, jc1 - jc0);
+  }
+  __device__ __forceinline__ bool has(int j) const { return j >= jc0 && j < jc1; }
+};
+
+// Sol decisions (threshold rule) for 32 query blocks of one (head, batch): three
+// passes over the key blocks, the mean, the population variance about it, then
+// the decisions.
+// Each wave takes every NW-th 32-block column tile.
+constexpr int kDecideWaves = 4;
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecideWaves) void decide_sol_kernel(RouteArgs a) {
+  constexpr int NW = kDecideWaves;
+  using PT = ProxyTiles<D>;
+  __shared__ double red[NW][32];
+  __shared__ double colsum[NW][32][33];   // per wave: [row][column lane], padded
+  __shared__ double mu_s[32], thr_s[32];
+  __shared__ int keep_s[32];
+  const DecideItem wi(a);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t bh = (int64_t)wi.b * a.H + wi.h;
+  const int i0 = wi.i0;
+  const PT pt(a, bh, i0, lane);
+  const int n = pt.n;
+  const CandRange cr(a);
+  const int N = cr.N;
+  const int t0 = cr.jc0 / 32, t1 = (cr.jc1 + 31) / 32;   // column tiles touching the candidates
   // per-row sum over the candidate columns of f(s, row), reduced over the workgroup into red[0][row]
   auto row_sum = [&](auto f) __attribute__((always_inline)) {
     double acc[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0;
-    KOps kn;
-    if (t0 + wave < t1) load_k(t0 + wave, kn);
+    typename PT::KOps kn;
+    if (t0 + wave < t1) pt.load_k(a, t0 + wave, kn);
     for (int tt = t0 + wave; tt < t1; tt += NW) {
-      const KOps kc = kn;
-      if (tt + NW < t1) load_k(tt + NW, kn);   // next tile's operands in flight
+      const typename PT::KOps kc = kn;
+      if (tt + NW < t1) pt.load_k(a, tt + NW, kn);   // next tile's operands in flight
       double sv[16];
-      tile(tt, kc, sv);
-      const int j = tt * 32 + n;
-      const bool cand = j >= jc0 && j < jc1;
+      pt.tile(a, tt, kc, sv);
+      const bool cand = cr.has(tt * 32 + n);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] += cand ? f(sv[e], row_of(e)) : 0.0;
+      for (int e = 0; e < 16; ++e) acc[e] += cand ? f(sv[e], pt.row_of(e)) : 0.0;
     }
     // over the 32 columns held by lanes with the same hf: through LDS
 #pragma unroll
-    for (int e = 0; e < 16; ++e) colsum[wave][row_of(e)][n] = acc[e];
+    for (int e = 0; e < 16; ++e) colsum[wave][pt.row_of(e)][n] = acc[e];
     __syncthreads();
     if (lane < 32) {
       double sum = 0.0;
@@ -344,20 +382,186 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_sol_kernel(RouteArgs
   for (int tt = wave; tt < nt; tt += NW) {
     const int j = tt * 32 + n;
     double sv[16];
-    const bool any_cand = tt * 32 + 31 >= jc0 && tt * 32 < jc1;
+    const bool any_cand = tt * 32 + 31 >= cr.jc0 && tt * 32 < cr.jc1;
     if (any_cand) {
-      KOps kc;
-      load_k(tt, kc);
-      tile(tt, kc, sv);
+      typename PT::KOps kc;
+      pt.load_k(a, tt, kc);
+      pt.tile(a, tt, kc, sv);
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int r = row_of(e), i = i0 + r;
+      const int r = pt.row_of(e), i = i0 + r;
       if (i >= a.nQB || j >= a.nKB) continue;
       uint8_t st;
-      if (j * kb >= a.lkv_valid) st = 0;
-      else if (j * kb < a.prefix) st = 1;
+      if (j * a.kblock >= a.lkv_valid) st = 0;
+      else if (j * a.kblock < a.prefix) st = 1;
       else st = (!keep_s[r] && sv[e] > thr_s[r]) ? 2 : 1;
+      a.map[(bh * a.nQB + i) * a.nKB + j] = st;
+    }
+  }
+}
+
+// Fixed-sparsity decisions (Ref2VA VSA, two-stage attention patch: top-k
+// pruning of the video key tiles at a set sparsity) for 32 query blocks of one
+// (head, batch).  With N candidates, each query block keeps the
+// keep = N - floor(sparsity * N) candidates of largest proxy; the rest become
+// centroids (G > 0) or are dropped (G = 0).
+//
+// Selection is an exact radix select on a 96-bit key per candidate: the
+// float64 proxy mapped to an order-preserving uint64 (with -0 taken as +0),
+// then the complement of the block index, so equal proxies rank the lower
+// index first and no two keys are equal.  Pass p histograms digit p (8 bits,
+// most significant first) of the keys that match the boundary prefix found so
+// far, 256 bins per query block in LDS; the bin holding the keep-th largest key
+// extends the prefix.  A query block is settled once that bin is kept whole
+// (at pass 12 at the latest, when the bin holds a single key); its kept
+// candidates are then exactly those whose key prefix is >= the boundary
+// prefix.  Proxies are recomputed on every pass.
+__device__ __forceinline__ uint64_t order_key(double s) {
+  const uint64_t u = (uint64_t)__double_as_longlong(s + 0.0);   // -0 + 0 = +0
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// First p digits (8 bits each) of the key (hi, lo) as integers: the top
+// min(p, 8) digits of hi, the top p - 8 digits of lo.
+__device__ __forceinline__ uint64_t key_hi_prefix(uint64_t hi, int p) {
+  return p == 0 ? 0ull : (p >= 8 ? hi : hi >> (64 - 8 * p));
+}
+__device__ __forceinline__ uint32_t key_lo_prefix(uint32_t lo, int p) {
+  return p <= 8 ? 0u : (p >= 12 ? lo : lo >> (32 - 8 * (p - 8)));
+}
+__device__ __forceinline__ uint32_t key_digit(uint64_t hi, uint32_t lo, int p) {
+  return p < 8 ? (uint32_t)(hi >> (56 - 8 * p)) & 255u : (lo >> (24 - 8 * (p - 8))) & 255u;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecideWaves) void decide_topk_kernel(RouteArgs a) {
+  constexpr int NW = kDecideWaves;
+  constexpr int kDigits = 12;
+  using PT = ProxyTiles<D>;
+  __shared__ uint32_t hist[32][256];
+  __shared__ uint64_t phi_s[32];   // boundary prefix: digits from the proxy
+  __shared__ uint32_t plo_s[32];   // boundary prefix: digits from the block index
+  __shared__ int dig_s[32];        // digits in the prefix
+  __shared__ int krem_s[32];       // kept keys still to place inside the prefix's bin
+  __shared__ int done_s[32];
+  const DecideItem wi(a);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t bh = (int64_t)wi.b * a.H + wi.h;
+  const int i0 = wi.i0;
+  const PT pt(a, bh, i0, lane);
+  const int n = pt.n;
+  const CandRange cr(a);
+  const int N = cr.N;
+  const int keep = N - (int)floor((double)a.sparsity * (double)N);
+  const uint8_t pruned = a.G > 0 ? 2 : 0;
+  const bool select = keep > 0 && keep < N;
+  if (t < 32) {
+    phi_s[t] = 0;
+    plo_s[t] = 0;
+    dig_s[t] = 0;
+    krem_s[t] = keep;
+    done_s[t] = (!select || i0 + t >= a.nQB) ? 1 : 0;
+    if (a.stats && i0 + t < a.nQB) {
+      a.stats[(bh * a.nQB + i0 + t) * 2] = __builtin_nan("");
+      a.stats[(bh * a.nQB + i0 + t) * 2 + 1] = __builtin_nan("");
+    }
+  }
+  const int t0 = cr.jc0 / 32, t1 = (cr.jc1 + 31) / 32;
+  if (select) {
+    for (int p = 0; p < kDigits; ++p) {
+      for (int x = t; x < 32 * 256; x += 256) (&hist[0][0])[x] = 0u;
+      __syncthreads();   // cleared bins and the previous pass's prefixes are visible
+      int active = 0;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) active += done_s[r] ? 0 : 1;
+      if (active == 0) break;   // same value in every thread
+      typename PT::KOps kn;
+      if (t0 + wave < t1) pt.load_k(a, t0 + wave, kn);
+      for (int tt = t0 + wave; tt < t1; tt += NW) {
+        const typename PT::KOps kc = kn;
+        if (tt + NW < t1) pt.load_k(a, tt + NW, kn);
+        double sv[16];
+        pt.tile(a, tt, kc, sv);
+        const int j = tt * 32 + n;
+        if (!cr.has(j)) continue;
+        const uint32_t lo = ~(uint32_t)j;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = pt.row_of(e);
+          if (done_s[r]) continue;
+          const uint64_t hi = order_key(sv[e]);
+          if (key_hi_prefix(hi, p) != phi_s[r] || key_lo_prefix(lo, p) != plo_s[r]) continue;
+          atomicAdd(&hist[r][key_digit(hi, lo, p)], 1u);
+        }
+      }
+      __syncthreads();
+      // boundary bin per unsettled query block: wave w scans rows 8w..8w+7,
+      // lane l holding bins 255-4l .. 252-4l (largest digits first)
+      for (int r = wave * 8; r < wave * 8 + 8; ++r) {
+        if (done_s[r]) continue;
+        uint32_t c4[4];
+        uint32_t own = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c4[q] = hist[r][255 - 4 * lane - q];
+          own += c4[q];
+        }
+        uint32_t incl = own;   // inclusive prefix over lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = __shfl_up(incl, off);
+          incl += lane >= off ? o : 0u;
+        }
+        const uint32_t k = (uint32_t)krem_s[r];
+        uint32_t above = incl - own;
+        if (above < k && k <= incl) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (above + c4[q] >= k) {
+              const uint32_t dgt = 255u - 4u * lane - q, kr = k - above;
+              if (p < 8) phi_s[r] = (phi_s[r] << 8) | dgt;
+              else plo_s[r] = (plo_s[r] << 8) | dgt;
+              dig_s[r] = p + 1;
+              krem_s[r] = (int)kr;
+              done_s[r] = c4[q] == kr ? 1 : 0;
+              break;
+            }
+            above += c4[q];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  // decisions for every key block
+  const int nt = (a.nKB + 31) / 32;
+  for (int tt = wave; tt < nt; tt += NW) {
+    const int j = tt * 32 + n;
+    double sv[16];
+    const bool any_cand = select && tt * 32 + 31 >= cr.jc0 && tt * 32 < cr.jc1;
+    if (any_cand) {
+      typename PT::KOps kc;
+      pt.load_k(a, tt, kc);
+      pt.tile(a, tt, kc, sv);
+    }
+    const uint32_t lo = ~(uint32_t)j;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = pt.row_of(e), i = i0 + r;
+      if (i >= a.nQB || j >= a.nKB) continue;
+      uint8_t st;
+      if (j * a.kblock >= a.lkv_valid) st = 0;
+      else if (j * a.kblock < a.prefix) st = 1;
+      else if (!select) st = keep > 0 ? 1 : pruned;
+      else {
+        const int pd = dig_s[r];
+        const uint64_t hi = order_key(sv[e]), hp = key_hi_prefix(hi, pd);
+        const bool ge = pd <= 8 ? hp >= phi_s[r]
+                                : (hp > phi_s[r] || (hp == phi_s[r] && key_lo_prefix(lo, pd) >= plo_s[r]));
+        st = ge ? 1 : pruned;
+      }
       a.map[(bh * a.nQB + i) * a.nKB + j] = st;
     }
   }
@@ -404,7 +608,9 @@ static hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
     }
   }
   if (sol) {
-    decide_sol_kernel<D><<<dim3((a.nQB + 31) / 32, a.H, a.B), 64 * kDecideWaves, 0, st>>>(a);
+    const dim3 grid((a.nQB + 31) / 32 * a.H * a.B);
+    if (a.rule == kRuleTopK) decide_topk_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);
+    else decide_sol_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);
   } else {
     decide_explicit_kernel<<<dim3(a.nQB, a.H, a.B), 256, 0, st>>>(a);
   }

@@ -9,6 +9,8 @@ namespace sa {
 constexpr int kQBlock = 128;     // query rows per routing block
 constexpr int kTile = 64;        // key rows per exact tile in the forward kernel
 constexpr int kMaxLogical = 16;  // virtual-KV logical slices passed by value
+constexpr int kRuleThreshold = 0;  // routing rules, as in the C ABI
+constexpr int kRuleTopK = 1;
 
 struct SrcMap {
   int32_t v[kMaxLogical];
@@ -43,7 +45,9 @@ struct RouteArgs {
   const int32_t* v_block_src;
   int B, H, Lq, Lkv, Lv, d, lq_valid, lkv_valid;
   int nQB, nKB, kblock, G, prefix, k_scale_rows, v_scale_rows, map_kblock;
-  float tau;
+  int rule;        // kRuleThreshold or kRuleTopK (routing rules without an explicit map)
+  float tau;       // threshold rule
+  float sparsity;  // fixed-sparsity rule: fraction of candidates pruned
   const uint8_t* explicit_map;
   uint8_t* map;
   float* kc;

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 enum sa_status {
   SA_OK = 0,
@@ -62,6 +62,12 @@ enum sa_status {
 
 /* Block-map states (one uint8 per (query block, key block)). */
 enum sa_block_state { SA_DROP = 0, SA_EXACT = 1, SA_CENTROID = 2 };
+
+/* Routing rules used when no explicit map is given. */
+enum sa_route_rule {
+  SA_RULE_THRESHOLD = 0, /* Sol: centroid iff proxy > mean + threshold * std */
+  SA_RULE_TOPK = 1       /* fixed sparsity: keep the best-scored candidates */
+};
 
 /* Element types for V and the attention output. */
 enum sa_dtype { SA_BF16 = 0, SA_INT8 = 1, SA_F32 = 2 };
@@ -87,6 +93,9 @@ typedef struct sa_route_params {
   int32_t k_scale_rows;        /* rows per K scale: 64 or 128 (== kblock for the Sol rule) */
   int32_t v_scale_rows;        /* rows per V scale when V is INT8: 64 or 128 */
   int32_t map_kblock;          /* key rows per entry of an explicit map: a multiple of kblock */
+  int32_t rule;                /* SA_RULE_THRESHOLD or SA_RULE_TOPK (ignored with an explicit map) */
+  float sparsity;              /* SA_RULE_TOPK: fraction of the candidates pruned per query
+                                  block, in [0, 1]; NaN or outside is rejected */
 } sa_route_params;
 
 /* ABI version of this build (SA_ABI_VERSION).  A caller compiled against another
@@ -137,24 +146,33 @@ size_t sparse_attn_route_workspace_size(const sa_dims* dims, const sa_route_para
  *   explicit_map NULL: Sol rule.  Else uint8 [B,H,Lq/128,Lkv/map_kblock]; values
  *             above 2, and centroid entries when G = 0, are taken as SA_EXACT.
  *   block_map out uint8 [B,H,Lq/128,Lkv/kblock]:
- *             Sol rule: candidates are key blocks with a valid row at or after
- *             the prefix; proxy s_ij = (sum of INT8 Q codes of query block i) .
+ *             Candidates are key blocks with a valid row at or after the
+ *             prefix; proxy s_ij = (sum of INT8 Q codes of query block i) .
  *             (sum of INT8 K codes of key block j) * b_j / n_j (n_j valid rows,
  *             b_j the block's K scale) — the dot of the dequantized block means
- *             up to a positive per-query-block factor; mu, sigma = mean and
- *             population std of s_ij over the candidates (float64);
- *             SA_CENTROID iff s_ij > mu + threshold*sigma, else SA_EXACT (all
- *             SA_EXACT if there are no candidates or sigma = 0).  Prefix blocks
- *             SA_EXACT; key blocks without valid rows SA_DROP (also for maps).
+ *             up to a positive per-query-block factor, exact in float64.
+ *             SA_RULE_THRESHOLD: mu, sigma = mean and population std of s_ij
+ *             over the candidates (float64); SA_CENTROID iff
+ *             s_ij > mu + threshold*sigma, else SA_EXACT (all SA_EXACT if there
+ *             are no candidates or sigma = 0).
+ *             SA_RULE_TOPK (Ref2VA VSA, two-stage attention patch: top-k
+ *             pruning of the video key tiles at a set sparsity): with N
+ *             candidates, the N - floor(sparsity * N) of largest s_ij (the
+ *             product in float64; equal s_ij ordered by lower block index) are
+ *             SA_EXACT, the others SA_CENTROID when G > 0 and SA_DROP when G = 0.
+ *             Prefix blocks SA_EXACT; key blocks without valid rows SA_DROP
+ *             (also for maps).
  *   k_centroid, v_centroid out fp32 [B,H,Lkv/kblock,G,d]; count out fp32
  *             [B,H,Lkv/kblock,G]: group g covers rows [g*kblock/G,(g+1)*kblock/G)
  *             of the block; kbar = mean of the dequantized INT8 keys, vbar =
  *             mean of V, count = valid rows (0 for an empty group).  Written for
  *             every block when G > 0; may be NULL when G = 0.
- *   row_stats optional out float64 [B,H,Lq/128,2] = (mu, sigma); NaN for maps.
+ *   row_stats optional out float64 [B,H,Lq/128,2] = (mu, sigma); NaN for maps
+ *             and for SA_RULE_TOPK.
  *   workspace device memory of sparse_attn_route_workspace_size() bytes.
- * Decisions are bit-exact with a float64 evaluation except where s_ij lies
- * within 1e-6*sigma of the threshold (summation order of mu, sigma). */
+ * Threshold decisions are bit-exact with a float64 evaluation except where s_ij
+ * lies within 1e-6*sigma of the threshold (summation order of mu, sigma);
+ * SA_RULE_TOPK decisions are bit-exact. */
 int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale, const void* v,
                           int32_t v_dtype, const float* v_scale, const int32_t* v_block_src,
                           const sa_dims* dims, const sa_route_params* p,

@@ -56,7 +56,8 @@ def gpu_pipeline(wl, tau=None, out_dtype=torch.float32, kblock=None, map_kblock=
                              v_block_src=vbs, threshold=tau, centroids_per_block=G,
                              prefix_tokens=wl.prefix_tokens, kblock=kblock, k_scale_rows=wl.k_scale_rows,
                              v_scale_rows=wl.v_scale_rows, explicit_map=em,
-                             map_kblock=map_kblock or wl.map_kblock, row_stats=True)
+                             map_kblock=map_kblock or wl.map_kblock, rule=wl.rule, sparsity=wl.sparsity,
+                             row_stats=True)
     out, lse = sa.sparse_attn_fwd(q8, qs, k8, ks, v_in, r["map"], k_centroid=r["k_centroid"],
                                   v_centroid=r["v_centroid"], count=r["count"], lq_valid=wl.lq_valid,
                                   lkv_valid=wl.lkv_valid, v_scale=vsc, v_block_src=vbs, centroids_per_block=G,

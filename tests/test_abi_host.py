@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 1
+    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 2
 
 
 def test_missing_library_lists_search_paths(monkeypatch, tmp_path):
@@ -90,10 +90,11 @@ def _dims(**kw):
 
 def _prm(**kw):
     d = dict(threshold=1.0, centroids_per_block=1, prefix_tokens=0, kblock=64, k_scale_rows=64, v_scale_rows=128,
-             map_kblock=64)
+             map_kblock=64, rule=sa.SA_RULE_THRESHOLD, sparsity=0.0)
     d.update(kw)
     return sa.sa_route_params(d["threshold"], *[d[k] for k in ("centroids_per_block", "prefix_tokens", "kblock",
-                                                                   "k_scale_rows", "v_scale_rows", "map_kblock")])
+                                                                   "k_scale_rows", "v_scale_rows", "map_kblock",
+                                                                   "rule", "sparsity")])
 
 
 def _route(dims, prm, em=None, ws=None, wsb=0, G_out=True):
@@ -115,6 +116,11 @@ def _route(dims, prm, em=None, ws=None, wsb=0, G_out=True):
     ({}, dict(centroids_per_block=0), sa.SA_E_VALUE, "centroids"),
     ({}, dict(centroids_per_block=3), sa.SA_E_VALUE, "centroids"),
     ({}, dict(k_scale_rows=128), sa.SA_E_VALUE, "k_scale_rows == kblock"),
+    ({}, dict(rule=2), sa.SA_E_VALUE, "rule must be"),
+    ({}, dict(rule=sa.SA_RULE_TOPK, sparsity=1.5), sa.SA_E_VALUE, "sparsity"),
+    ({}, dict(rule=sa.SA_RULE_TOPK, sparsity=-0.25), sa.SA_E_VALUE, "sparsity"),
+    ({}, dict(rule=sa.SA_RULE_TOPK, sparsity=float("nan")), sa.SA_E_VALUE, "sparsity"),
+    ({}, dict(rule=sa.SA_RULE_TOPK, sparsity=0.5, k_scale_rows=128), sa.SA_E_VALUE, "k_scale_rows == kblock"),
 ])
 def test_route_validation(dims_kw, prm_kw, code, msg):
     assert _route(_dims(**dims_kw), _prm(**prm_kw)) == code
@@ -179,3 +185,15 @@ def test_gather_validation():
     assert lib.gather_virtual_kv(p, 1, 2, 2048, 2, 128, src_ok, 7, p, p, 1, 44, 64, p, p, p, None) == sa.SA_E_VALUE
     assert lib.gather_virtual_kv(p, 1, 2, 2000, 2, 128, src_ok, 7, p, p, 0, 44, 64, p, p, p, None) == sa.SA_E_SHAPE
     assert lib.gather_virtual_kv(p, 1, 2, 2048, 2, 128, src_ok, 7, p, p, 100, 44, 64, p, p, p, None) == sa.SA_E_VALUE
+
+
+def test_topk_rule_without_centroids_passes_validation():
+    """The fixed-sparsity rule accepts G = 0 (pruned blocks are dropped) and then
+    needs no centroid outputs; without a GPU the call stops at the device check."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("dummy pointers: meaningful only without a GPU")
+    dims, prm = _dims(), _prm(rule=sa.SA_RULE_TOPK, sparsity=0.75, centroids_per_block=0)
+    need = _lib().sparse_attn_route_workspace_size(ctypes.byref(dims), ctypes.byref(prm), 0)
+    assert need > 0
+    assert _route(dims, prm, ws=ctypes.c_void_p(256), wsb=need, G_out=False) == sa.SA_E_DEVICE

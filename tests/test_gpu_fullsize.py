@@ -78,3 +78,20 @@ def test_full_sol_prefix_2x32(sa, orc):
 def test_full_virtual_kv_residual(sa, orc):
     wl = W.config(5)
     _check_workload(orc, wl, sel=_sample(wl, 24, 5))
+
+
+def test_full_wan14b_like_topk(sa, orc):
+    """Fixed-sparsity routing at 0.75 (Ref2VA VSA recipe) on the 32K workload:
+    the whole map bit-exact, outputs on sampled query blocks."""
+    wl = W.config(3)
+    wl.rule, wl.sparsity = 1, 0.75
+    g, o = _check_workload(orc, wl, sel=_sample(wl, 12, 6, frame_tokens=30 * 52))
+    nvalid = -(-wl.lkv_valid // 64)
+    kept = (g["map"][..., :nvalid] == 1).sum(-1)
+    assert (kept == nvalid - int(np.floor(0.75 * nvalid))).all()
+
+
+def test_full_sol_prefix_topk_2x32(sa, orc):
+    wl = W.config(4)
+    wl.rule, wl.sparsity = 1, 0.6
+    _check_workload(orc, wl, sel=_sample(wl, 12, 7, frame_tokens=84 * 48, prefix=1024))

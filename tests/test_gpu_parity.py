@@ -234,3 +234,35 @@ def test_saturated_block_sums(sa, orc):
     # the saturated blocks really are at the extreme
     assert np.abs(o["q8"][0, 0, :128].astype(np.int32).sum(axis=0)).max() == 127 * 128
     assert np.abs(o["k8"][0, 0, 384:512].astype(np.int32).sum(axis=0)).max() == 127 * 128
+
+
+@pytest.mark.parametrize("d,G,sparsity,kblock", [(128, 1, 0.75, 64), (128, 2, 0.5, 64), (64, 1, 0.6, 64),
+                                                 (128, 0, 0.75, 64), (128, 1, 0.7, 128), (64, 1, 0.0, 64),
+                                                 (128, 2, 1.0, 64)])
+def test_topk_routing(sa, orc, d, G, sparsity, kblock):
+    """Fixed-sparsity rule: bit-exact map (no tie band), then the forward pass
+    over it; G = 0 drops the pruned blocks."""
+    wl = W.tiny_sol(seed=31, H=2, L=1024, d=d, valid=1000, centroids_per_block=max(G, 1))
+    wl.centroids_per_block = G
+    wl.rule, wl.sparsity = 1, sparsity
+    wl.kblock = wl.k_scale_rows = kblock
+    g, o = _check_workload(orc, wl)
+    assert np.isnan(g["stats"]).all()
+
+
+def test_topk_equal_scores(sa, orc):
+    """Identical key blocks give equal proxies: the kept blocks are the lowest
+    indices, on the GPU as in the oracle."""
+    wl = W.tiny_sol(seed=32, H=2, L=1024, d=128, centroids_per_block=1)
+    k = wl.k.copy()
+    k[:, :, :, :] = np.tile(k[:, :, :64, :], (1, 1, 16, 1))
+    wl.k = k
+    wl.rule, wl.sparsity = 1, 0.75
+    g, o = _check_workload(orc, wl)
+    assert (g["map"][..., :4] == 1).all() and (g["map"][..., 4:] == 2).all()
+
+
+def test_topk_prefix(sa, orc):
+    wl = W.config(4, small=True)
+    wl.rule, wl.sparsity = 1, 0.75
+    _check_workload(orc, wl)
