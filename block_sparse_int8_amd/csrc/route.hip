@@ -567,6 +567,202 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_topk_kernel(RouteArg
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decisions with the proxies held in LDS.  When a query block has at most
+// kLdsCand candidates, one pass of matrix-core tiles writes s_ij for the 32
+// query blocks of a workgroup into a 32 x kLdsCand float64 array (128 KiB),
+// and every later pass reads it from there.  The rules and their arithmetic are
+// those of the kernels above; only where s lives changes (and the summation
+// order of the mean and variance).  One workgroup per CU; kLdsWaves waves.
+// ---------------------------------------------------------------------------
+constexpr int kLdsCand = 512;
+constexpr int kLdsWaves = 8;
+
+template <int D, int NW>
+__device__ __forceinline__ void proxies_to_lds(const RouteArgs& a, const ProxyTiles<D>& pt, const CandRange& cr,
+                                               int wave, double (*sv_s)[kLdsCand]) {
+  const int t0 = cr.jc0 / 32, t1 = (cr.jc1 + 31) / 32;
+  typename ProxyTiles<D>::KOps kn;
+  if (t0 + wave < t1) pt.load_k(a, t0 + wave, kn);
+  for (int tt = t0 + wave; tt < t1; tt += NW) {
+    const typename ProxyTiles<D>::KOps kc = kn;
+    if (tt + NW < t1) pt.load_k(a, tt + NW, kn);
+    double sv[16];
+    pt.tile(a, tt, kc, sv);
+    const int j = tt * 32 + pt.n;
+    if (!cr.has(j)) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sv_s[pt.row_of(e)][j - cr.jc0] = sv[e];
+  }
+}
+
+// Block states of query block i0 + r for every key block, one coalesced row of
+// bytes at a time: DROP past the valid keys, EXACT in the prefix, cand_state(c)
+// for candidate c.
+template <typename F>
+__device__ __forceinline__ void write_map_rows(const RouteArgs& a, int64_t bh, int i0, const CandRange& cr, int nt,
+                                               F cand_state) {
+  for (int r = 0; r < 32 && i0 + r < a.nQB; ++r) {
+    uint8_t* mrow = a.map + (bh * a.nQB + i0 + r) * a.nKB;
+    for (int j = threadIdx.x; j < a.nKB; j += nt) {
+      uint8_t st;
+      if (j * a.kblock >= a.lkv_valid) st = 0;
+      else if (j * a.kblock < a.prefix) st = 1;
+      else st = cand_state(r, j - cr.jc0);
+      mrow[j] = st;
+    }
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
+  constexpr int NT = 64 * NW, TPR = NT / 32;   // threads per query-block row
+  __shared__ double sv_s[32][kLdsCand];
+  __shared__ double thr_s[32];
+  __shared__ int keep_s[32];
+  const DecideItem wi(a);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t bh = (int64_t)wi.b * a.H + wi.h;
+  const int i0 = wi.i0;
+  const ProxyTiles<D> pt(a, bh, i0, lane);
+  const CandRange cr(a);
+  const int N = cr.N;
+  proxies_to_lds<D, NW>(a, pt, cr, wave, sv_s);
+  __syncthreads();
+  // row r's mean and population variance: TPR adjacent lanes per row
+  const int r = t / TPR, part = t % TPR;
+  double acc = 0.0;
+  for (int c = part; c < N; c += TPR) acc += sv_s[r][c];
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  const double mu = N > 0 ? acc / N : __builtin_nan("");
+  double acc2 = 0.0;
+  for (int c = part; c < N; c += TPR) {
+    const double dl = sv_s[r][c] - mu;
+    acc2 += dl * dl;
+  }
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) acc2 += __shfl_xor(acc2, o, 64);
+  if (part == 0) {
+    const double tau = (double)a.tau;
+    const double sigma = N > 0 ? sqrt(acc2 / N) : __builtin_nan("");
+    const bool keep_all = N == 0 || (tau > 0 && __builtin_isinf(tau)) || sigma == 0.0;
+    keep_s[r] = keep_all ? 1 : 0;
+    thr_s[r] = keep_all ? 0.0 : mu + tau * sigma;
+    if (a.stats && i0 + r < a.nQB) {
+      a.stats[(bh * a.nQB + i0 + r) * 2] = mu;
+      a.stats[(bh * a.nQB + i0 + r) * 2 + 1] = sigma;
+    }
+  }
+  __syncthreads();
+  write_map_rows(a, bh, i0, cr, NT, [&](int rr, int c) -> uint8_t {
+    return (!keep_s[rr] && sv_s[rr][c] > thr_s[rr]) ? 2 : 1;
+  });
+}
+
+// Fixed-sparsity decisions with LDS-resident proxies.  The keep-th largest
+// 96-bit key of a query block (the same keys as decide_topk_kernel) is found
+// bit by bit inside one wave: lane l holds candidates l, l+64, ... of the row
+// in registers, and each step counts, with one ballot per register, the keys
+// that match the prefix so far and have a 1 in the next bit.  If at least
+// `remaining` do, the bit is 1; otherwise it is 0 and those keys are all kept.
+// The row is settled when every key matching the prefix is kept (at bit 96 at
+// the latest, where one key matches).  No atomics and no barriers.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
+  constexpr int NT = 64 * NW;
+  constexpr int NV = kLdsCand / 64;   // candidates per lane
+  __shared__ double sv_s[32][kLdsCand];
+  __shared__ uint64_t phi_s[32];
+  __shared__ uint32_t plo_s[32];
+  __shared__ int nb_s[32];
+  const DecideItem wi(a);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t bh = (int64_t)wi.b * a.H + wi.h;
+  const int i0 = wi.i0;
+  const CandRange cr(a);
+  const int N = cr.N;
+  const int keep = N - (int)floor((double)a.sparsity * (double)N);
+  const uint8_t pruned = a.G > 0 ? 2 : 0;
+  const bool select = keep > 0 && keep < N;
+  if (t < 32 && a.stats && i0 + t < a.nQB) {
+    a.stats[(bh * a.nQB + i0 + t) * 2] = __builtin_nan("");
+    a.stats[(bh * a.nQB + i0 + t) * 2 + 1] = __builtin_nan("");
+  }
+  if (select) {
+    const ProxyTiles<D> pt(a, bh, i0, lane);
+    proxies_to_lds<D, NW>(a, pt, cr, wave, sv_s);
+    __syncthreads();
+    for (int r = wave; r < 32; r += NW) {
+      if (i0 + r >= a.nQB) break;
+      // the key of each register in three 32-bit words, most significant first;
+      // which lanes still match the prefix, one wave mask per register
+      uint32_t w0[NV], w1[NV], w2[NV];
+      uint64_t live[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int c = lane + 64 * k;
+        const uint64_t hk = c < N ? order_key(sv_s[r][c]) : 0ull;
+        w0[k] = (uint32_t)(hk >> 32);
+        w1[k] = (uint32_t)hk;
+        w2[k] = ~(uint32_t)(cr.jc0 + c);
+        live[k] = __ballot(c < N);
+      }
+      int m = N, rem = keep, nb = 0;
+      uint64_t ph = 0;
+      uint32_t pl = 0;
+      // one bit per step; the word is shifted so that the bit is its sign
+      auto phase = [&](uint32_t (&w)[NV]) __attribute__((always_inline)) {
+        for (int step = 0; step < 32 && m != rem; ++step, ++nb) {
+          uint64_t ones[NV];
+          int c1 = 0;
+#pragma unroll
+          for (int k = 0; k < NV; ++k) {
+            ones[k] = __ballot((int32_t)w[k] < 0) & live[k];
+            c1 += __popcll(ones[k]);
+            w[k] <<= 1;
+          }
+          const bool one = c1 >= rem;
+          if (one) {
+            m = c1;
+          } else {
+            rem -= c1;
+            m -= c1;
+          }
+#pragma unroll
+          for (int k = 0; k < NV; ++k) live[k] = one ? ones[k] : live[k] & ~ones[k];
+          if (nb < 64) ph = (ph << 1) | (one ? 1ull : 0ull);
+          else pl = (pl << 1) | (one ? 1u : 0u);
+        }
+      };
+      phase(w0);
+      phase(w1);
+      phase(w2);
+      if (lane == 0) {
+        phi_s[r] = ph;
+        plo_s[r] = pl;
+        nb_s[r] = nb;
+      }
+    }
+  }
+  __syncthreads();
+  // kept iff the key's first nb bits are >= the boundary prefix
+  write_map_rows(a, bh, i0, cr, NT, [&](int r, int c) -> uint8_t {
+    if (!select) return keep > 0 ? 1 : pruned;
+    const int nb = nb_s[r];
+    const uint64_t hi = order_key(sv_s[r][c]);
+    const uint32_t lo = ~(uint32_t)(cr.jc0 + c);
+    bool ge;
+    if (nb <= 64) {
+      ge = nb == 0 || (hi >> (64 - nb)) >= phi_s[r];
+    } else {
+      const uint32_t lp = nb == 96 ? lo : lo >> (96 - nb);
+      ge = hi > phi_s[r] || (hi == phi_s[r] && lp >= plo_s[r]);
+    }
+    return ge ? 1 : pruned;
+  });
+}
+
 __global__ __launch_bounds__(256) void decide_explicit_kernel(RouteArgs a) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int64_t bh = (int64_t)b * a.H + h;
@@ -609,8 +805,16 @@ static hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
   }
   if (sol) {
     const dim3 grid((a.nQB + 31) / 32 * a.H * a.B);
-    if (a.rule == kRuleTopK) decide_topk_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);
-    else decide_sol_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);
+    const int jc0 = (a.prefix + a.kblock - 1) / a.kblock;
+    const int jc1 = min(a.nKB, (a.lkv_valid + a.kblock - 1) / a.kblock);
+    const bool lds = jc1 - jc0 <= kLdsCand;   // candidates' proxies fit in LDS
+    if (a.rule == kRuleTopK) {
+      if (lds) decide_topk_lds_kernel<D, kLdsWaves><<<grid, 64 * kLdsWaves, 0, st>>>(a);
+      else decide_topk_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);
+    } else {
+      if (lds) decide_sol_lds_kernel<D, kLdsWaves><<<grid, 64 * kLdsWaves, 0, st>>>(a);
+      else decide_sol_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);
+    }
   } else {
     decide_explicit_kernel<<<dim3(a.nQB, a.H, a.B), 256, 0, st>>>(a);
   }
