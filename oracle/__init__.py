@@ -60,12 +60,20 @@ def quantize(x_bits: np.ndarray, valid_len: Optional[int] = None, rows_per_block
     return q, s
 
 
+def _segments(segments):
+    if segments is None or len(segments) == 0:
+        return None
+    return np.ascontiguousarray(np.asarray(segments, dtype=np.int32).reshape(-1, 3))
+
+
 def route(q8, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, *, v_bits=None, v8=None, v_scale=None,
           v_scale_rows=128, v_block_src=None, tau=1.0, G=1, prefix=0, kblock=64,
-          explicit_map=None, map_kblock=None, rule=0, sparsity=0.0):
+          explicit_map=None, map_kblock=None, rule=0, sparsity=0.0, segments=None):
     """Block map, centroids and routing statistics for one attention call.
     ``rule`` 0 is the threshold rule (``tau``), 1 the fixed-sparsity rule
     (``sparsity``, taken at float32 precision as the library's parameter is).
+    ``segments`` (int [n, 3]: start, rows, routed) describes the key layout in
+    place of ``prefix``.
     Returns a dict with map uint8 [B,H,nQB,nKB], kbar/vbar float64
     [B,H,nKB,G,d], count float64 [B,H,nKB,G], stats float64 [B,H,nQB,2]
     (mu, sigma; NaN for explicit maps and the fixed-sparsity rule) and tie
@@ -99,10 +107,12 @@ def route(q8, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, *, v_bits=None, v8
             map_kblock = kblock
         if em.shape != (B, H, nQB, -(-Lkv // map_kblock)):
             raise ValueError(f"explicit map shape {em.shape}")
+    sg = _segments(segments)
     rc = _lib().orc_route(_p(q8), _p(k8), _p(ks), k_scale_rows, _p(vb), _p(vi), _p(vsc), v_scale_rows,
                           _p(vbs), Lv, B, H, Lq, Lkv, d, lq_valid, lkv_valid, int(rule), ctypes.c_double(tau),
                           ctypes.c_double(float(np.float32(sparsity))), G,
-                          prefix, kblock, _p(em), map_kblock or kblock, _p(out_map), _p(kbar), _p(vbar),
+                          prefix, kblock, _p(sg), 0 if sg is None else len(sg), _p(em), map_kblock or kblock,
+                          _p(out_map), _p(kbar), _p(vbar),
                           _p(count), _p(stats), _p(tie))
     if rc != 0:
         raise ValueError("oracle route rejected its arguments")
@@ -111,7 +121,8 @@ def route(q8, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, *, v_bits=None, v8
 
 def forward(q8, q_scale, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, block_map, *, kbar=None,
             vbar=None, count=None, v_bits=None, v8=None, v_scale=None, v_scale_rows=128,
-            v_block_src=None, kblock=64, G=1, sm_scale=None, sel: Optional[Sequence[int]] = None):
+            v_block_src=None, kblock=64, G=1, sm_scale=None, sel: Optional[Sequence[int]] = None,
+            segments=None):
     """Attention output for the selected query blocks (all when ``sel`` is None).
     ``sel`` entries are (b*H + h)*nQB + i.  Returns (out float64 [nsel,128,d],
     lse float64 [nsel,128], sel)."""
@@ -137,9 +148,11 @@ def forward(q8, q_scale, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, block_m
         vbar = np.zeros((B, H, nKB, Gs, d))
         count = np.zeros((B, H, nKB, Gs))
     sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+    sg = _segments(segments)
     _lib().orc_forward(_p(q8), _p(np.ascontiguousarray(q_scale, dtype=np.float32)), _p(k8),
                        _p(np.ascontiguousarray(k_scale, dtype=np.float32)), k_scale_rows, _p(vb), _p(vi),
-                       _p(vsc), v_scale_rows, _p(vbs), Lv, B, H, Lq, Lkv, d, lq_valid, lkv_valid, kblock, G,
+                       _p(vsc), v_scale_rows, _p(vbs), Lv, B, H, Lq, Lkv, d, lq_valid, lkv_valid, kblock,
+                       _p(sg), 0 if sg is None else len(sg), G,
                        _p(np.ascontiguousarray(block_map, dtype=np.uint8)),
                        _p(np.ascontiguousarray(kbar, dtype=np.float64)),
                        _p(np.ascontiguousarray(vbar, dtype=np.float64)),
@@ -203,9 +216,10 @@ def run(wl, sel=None, tau=None):
     r = route(q8, k8, ks, wl.k_scale_rows, wl.lq_valid, wl.lkv_valid, v_block_src=vbs, tau=tau,
               G=wl.centroids_per_block, prefix=wl.prefix_tokens, kblock=wl.kblock,
               explicit_map=wl.explicit_map, map_kblock=wl.map_kblock, rule=wl.rule, sparsity=wl.sparsity,
-              **vkw)
+              segments=wl.segments, **vkw)
     out, lse, sel = forward(q8, qs, k8, ks, wl.k_scale_rows, wl.lq_valid, wl.lkv_valid, r["map"],
                             kbar=r["kbar"], vbar=r["vbar"], count=r["count"], v_block_src=vbs,
-                            kblock=wl.kblock, G=wl.centroids_per_block, sm_scale=wl.sm_scale, sel=sel, **vkw)
+                            kblock=wl.kblock, G=wl.centroids_per_block, sm_scale=wl.sm_scale, sel=sel,
+                            segments=wl.segments, **vkw)
     return dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, v_block_src=vbs, out=out, lse=lse, sel=sel, **r,
                 **{k: v for k, v in vkw.items() if k != "v_bits"})

@@ -129,15 +129,58 @@ static double v_at(const orc_vsrc* s, int b, int h, int r, int c) {
 }
 
 /* ------------------------------------------------------------------------- */
+/* Key layout.  Ref2VA VSA, two-stage attention patch: the geometry mapper    */
+/* gives the text, reference-image and reference-audio tokens tiles of their */
+/* own, which stay dense, and only the generated-video key tiles are pruned; */
+/* Configure Sol Sparse Attention, "The inputs that matter": a long reference */
+/* video may be sparsified while images and audio stay exact, and the auto   */
+/* prefix policy follows the model's own layout.                             */
+/* seg holds nseg (start, rows, routed) triplets in increasing start, each   */
+/* start a multiple of the key block, so no key block spans two segments.   */
+/* Key row u is valid when it lies in [start, start + rows) of a segment and */
+/* below lkv_valid; the rest (a segment's padding up to the next start) is   */
+/* excluded like the padding at the end.  Key block j is routed when the     */
+/* segment holding its first row is.  Without segments (nseg = 0) the rows   */
+/* below lkv_valid are valid and blocks at or after the protected prefix are */
+/* routed.                                                                    */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+  const int32_t* seg;
+  int nseg, lkv_valid, prefix, kblock;
+} orc_layout;
+
+/* Segment holding row u (the last with start <= u), or -1. */
+static int orc_seg_of(const orc_layout* L, int u) {
+  int s = -1;
+  for (int x = 0; x < L->nseg; ++x)
+    if (L->seg[3 * x] <= u) s = x;
+  return s;
+}
+
+static int orc_key_valid(const orc_layout* L, int u) {
+  if (u >= L->lkv_valid) return 0;
+  if (L->nseg == 0) return 1;
+  int s = orc_seg_of(L, u);
+  return s >= 0 && u < L->seg[3 * s] + L->seg[3 * s + 1];
+}
+
+static int orc_block_routed(const orc_layout* L, int j) {
+  if (L->nseg == 0) return j * L->kblock >= L->prefix;
+  int s = orc_seg_of(L, j * L->kblock);
+  return s >= 0 && L->seg[3 * s + 2] != 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Routing: block map, centroids, statistics.                                 */
 /*                                                                            */
 /* Sums (integer): Qsum_i = sum of INT8 Q codes over the valid rows of query */
 /* block i; Ksum_j likewise over key block j; n_j = valid rows of key block. */
 /*                                                                            */
-/* Candidates of a query block: key blocks with at least one valid row that  */
-/* lie at or after the protected prefix (Configure Sol Sparse Attention, "The*/
-/* inputs that matter"; Ref2VA VSA, two-stage attention patch: only video key */
-/* tiles are pruned).  Prefix blocks are always exact, empty blocks dropped. */
+/* Candidates of a query block: routed key blocks (see the key layout) with */
+/* at least one valid row (Configure Sol Sparse Attention, "The inputs that */
+/* matter"; Ref2VA VSA, two-stage attention patch: only video key tiles are */
+/* pruned).  Other blocks with valid rows are always exact (the protected   */
+/* prefix, dense segments); blocks without valid rows are dropped.          */
 /*                                                                            */
 /* Proxy: the dot product of the dequantized block means, q_mean . k_mean.   */
 /* Dividing out the positive per-row factor a_i / n_i leaves                 */
@@ -195,6 +238,7 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
               const uint16_t* v_bf16, const int8_t* v_i8, const float* v_scale, int v_scale_rows,
               const int32_t* v_block_src, int Lv, int B, int H, int Lq, int Lkv, int d, int lq_valid,
               int lkv_valid, int rule, double tau, double sparsity, int G, int prefix, int kblock,
+              const int32_t* seg, int nseg,
               const uint8_t* explicit_map, int map_kblock, uint8_t* map, double* kbar,
               double* vbar, double* count, double* stats, uint8_t* tie) {
   int nQB = (Lq + QBLOCK - 1) / QBLOCK;
@@ -207,7 +251,13 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
   if (!explicit_map && rule == 1 && !(sparsity >= 0.0 && sparsity <= 1.0)) return -1;
   if (!explicit_map && rule != 0 && rule != 1) return -1;
   orc_vsrc vs = {v_bf16, v_i8, v_scale, v_scale_rows, v_block_src, Lv, H, d};
+  orc_layout lay = {seg, nseg, lkv_valid, prefix, kblock};
   int ok = 0;
+  for (int x = 0; x < nseg; ++x) {
+    if (seg[3 * x] % kblock || seg[3 * x + 1] < 0) return -1;
+    if (x > 0 && seg[3 * x] < seg[3 * (x - 1)] + seg[3 * (x - 1) + 1]) return -1;
+  }
+  if (nseg > 0 && prefix != 0) return -1;
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b)
@@ -224,7 +274,8 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
         for (int t = i * QBLOCK; t < (i + 1) * QBLOCK && t < Lq && t < lq_valid; ++t)
           for (int c = 0; c < d; ++c) Qs[(int64_t)i * d + c] += qh[(int64_t)t * d + c];
       for (int j = 0; j < nKB; ++j)
-        for (int u = j * kblock; u < (j + 1) * kblock && u < Lkv && u < lkv_valid; ++u) {
+        for (int u = j * kblock; u < (j + 1) * kblock && u < Lkv; ++u) {
+          if (!orc_key_valid(&lay, u)) continue;
           nk[j] += 1;
           for (int c = 0; c < d; ++c) Ks[(int64_t)j * d + c] += kh[(int64_t)u * d + c];
         }
@@ -240,7 +291,8 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
               kbar[o * d + c] = 0.0;
               vbar[o * d + c] = 0.0;
             }
-            for (int u = j * kblock + g * gr; u < j * kblock + (g + 1) * gr && u < Lkv && u < lkv_valid; ++u) {
+            for (int u = j * kblock + g * gr; u < j * kblock + (g + 1) * gr && u < Lkv; ++u) {
+              if (!orc_key_valid(&lay, u)) continue;
               ++n;
               double ks = (double)k_scale[bh * nKS + u / k_scale_rows];
               for (int c = 0; c < d; ++c) {
@@ -266,14 +318,14 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
           for (int j = 0; j < nKB; ++j) {
             int st = erow[(int64_t)j * kblock / map_kblock];
             if (st > ORC_CENTROID || (st == ORC_CENTROID && G == 0)) st = ORC_EXACT;
-            if (j * kblock < prefix) st = ORC_EXACT;
+            if (!orc_block_routed(&lay, j)) st = ORC_EXACT;
             if (nk[j] == 0) st = ORC_DROP;
             mrow[j] = (uint8_t)st;
           }
         } else {
           int N = 0;
           for (int j = 0; j < nKB; ++j) {
-            int cand = nk[j] > 0 && j * kblock >= prefix;
+            int cand = nk[j] > 0 && orc_block_routed(&lay, j);
             if (!cand) {
               mrow[j] = nk[j] > 0 ? ORC_EXACT : ORC_DROP;
               continue;
@@ -287,7 +339,7 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
             /* fixed sparsity: keep the N - floor(sparsity * N) best-scored */
             int n = 0;
             for (int j = 0; j < nKB; ++j)
-              if (nk[j] > 0 && j * kblock >= prefix) {
+              if (nk[j] > 0 && orc_block_routed(&lay, j)) {
                 ranked[n].s = s[j];
                 ranked[n].j = j;
                 ++n;
@@ -304,17 +356,17 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
           if (N > 0) {
             double sum = 0.0;
             for (int j = 0; j < nKB; ++j)
-              if (nk[j] > 0 && j * kblock >= prefix) sum += s[j];
+              if (nk[j] > 0 && orc_block_routed(&lay, j)) sum += s[j];
             mu = sum / N;
             double ss = 0.0;
             for (int j = 0; j < nKB; ++j)
-              if (nk[j] > 0 && j * kblock >= prefix) ss += (s[j] - mu) * (s[j] - mu);
+              if (nk[j] > 0 && orc_block_routed(&lay, j)) ss += (s[j] - mu) * (s[j] - mu);
             sigma = sqrt(ss / N);
           }
           int keep_all = N == 0 || (isinf(tau) && tau > 0) || sigma == 0.0;
           double thr = keep_all ? INFINITY : mu + tau * sigma;
           for (int j = 0; j < nKB; ++j) {
-            if (!(nk[j] > 0 && j * kblock >= prefix)) continue;
+            if (!(nk[j] > 0 && orc_block_routed(&lay, j))) continue;
             mrow[j] = (!keep_all && s[j] > thr) ? ORC_CENTROID : ORC_EXACT;
             if (trow && !keep_all && isfinite(thr) && fabs(s[j] - thr) <= 1e-6 * sigma) trow[j] = 1;
           }
@@ -354,7 +406,8 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
 void orc_forward(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                  int k_scale_rows, const uint16_t* v_bf16, const int8_t* v_i8, const float* v_scale,
                  int v_scale_rows, const int32_t* v_block_src, int Lv, int B, int H, int Lq, int Lkv,
-                 int d, int lq_valid, int lkv_valid, int kblock, int G, const uint8_t* map,
+                 int d, int lq_valid, int lkv_valid, int kblock, const int32_t* seg, int nseg, int G,
+                 const uint8_t* map,
                  const double* kbar, const double* vbar, const double* count, double sm_scale,
                  const int64_t* sel, int nsel, double* out, double* lse) {
   int nQB = (Lq + QBLOCK - 1) / QBLOCK;
@@ -362,6 +415,7 @@ void orc_forward(const int8_t* q, const float* q_scale, const int8_t* k, const f
   int nKS = (Lkv + k_scale_rows - 1) / k_scale_rows;
   int maxcols = Lkv + nKB * (G > 0 ? G : 0);
   orc_vsrc vs = {v_bf16, v_i8, v_scale, v_scale_rows, v_block_src, Lv, H, d};
+  orc_layout lay = {seg, nseg, lkv_valid, 0, kblock};
   (void)B;
 
 #pragma omp parallel
@@ -388,7 +442,8 @@ void orc_forward(const int8_t* q, const float* q_scale, const int8_t* k, const f
         int n = 0;
         for (int j = 0; j < nKB; ++j) {
           if (mrow[j] == ORC_EXACT) {
-            for (int u = j * kblock; u < (j + 1) * kblock && u < Lkv && u < lkv_valid; ++u) {
+            for (int u = j * kblock; u < (j + 1) * kblock && u < Lkv; ++u) {
+              if (!orc_key_valid(&lay, u)) continue;
               const int8_t* ku = k + (bh * Lkv + u) * d;
               int64_t dot = 0;
               for (int c = 0; c < d; ++c) dot += (int64_t)qt[c] * ku[c];

@@ -66,6 +66,7 @@ class Workload:
     sparsity: float = 0.0              # fraction of candidates pruned under the fixed-sparsity rule
     centroids_per_block: int = 1
     prefix_tokens: int = 0
+    segments: Optional[np.ndarray] = None      # int32 [n, 3] key layout: start, rows, routed (replaces the prefix)
     kblock: int = 64
     k_scale_rows: int = 64
     v_int8: bool = False               # V handed over as an INT8 cache (quantized per v_scale_rows)
@@ -254,6 +255,52 @@ def virtual_kv_residual(seed: int = 5, H: int = 24, rows_per_slice: int = 2048, 
                     centroids_per_block=2, kblock=64, k_scale_rows=64, explicit_map=emap, map_kblock=64,
                     virtual=True, rows_per_slice=rows_per_slice, n_phys=n_phys, src_map=src,
                     rope_cos=cos, rope_sin=sin, rot_offset=0, d_rot=d_rot)
+
+
+def ref2va_segments(seed: int = 6, H: int = 24, text: int = 77, ref_image: int = 30 * 52, ref_audio: int = 250,
+                    ref_video_frames: int = 2, video_frames: int = 8, frame_tokens: int = 30 * 52, d: int = 128,
+                    kblock: int = 64, sparse_reference_video: bool = True, threshold: float = 1.0,
+                    centroids_per_block: int = 1) -> Workload:
+    """Reference-conditioned video self-attention over a segmented key layout
+    (Ref2VA VSA, two-stage attention patch; Configure Sol Sparse Attention, "The
+    inputs that matter"): prompt text, a reference image and reference audio
+    (dense), a reference video clip (routed when ``sparse_reference_video``),
+    then the generated video (routed).  Each segment starts on a key-block
+    boundary; the rows between its end and the next start are zero padding, as
+    are the rows after the last segment up to a multiple of 128.
+    Draw order: text, reference image, reference audio (each Q, K, V i.i.d.
+    N(0,1)), then all video frames (reference clip first) like ``wan_like``."""
+    rng = np.random.default_rng(seed)
+    dense = []
+    for rows in (text, ref_image, ref_audio):
+        dense.append(tuple(iid_normal_bf16(rng, (H, rows, d)) for _ in range(3)))
+    nf = ref_video_frames + video_frames
+    qv, shared = framed_lowrank_bf16(rng, H, frame_tokens, nf, d)
+    kv, _ = framed_lowrank_bf16(rng, H, frame_tokens, nf, d, shared=shared)
+    vv, _ = framed_lowrank_bf16(rng, H, frame_tokens, nf, d)
+    cut = ref_video_frames * frame_tokens
+    parts = dense + [(qv[:, :cut], kv[:, :cut], vv[:, :cut]), (qv[:, cut:], kv[:, cut:], vv[:, cut:])]
+    routed = [0, 0, 0, 1 if sparse_reference_video else 0, 1]
+    segs, cursor = [], 0
+    for (pq, _, _), rt in zip(parts, routed):
+        rows = pq.shape[1]
+        if rows == 0:
+            continue
+        segs.append((cursor, rows, rt))
+        cursor += -(-rows // kblock) * kblock
+    L = -(-cursor // 128) * 128
+    q = np.zeros((1, H, L, d), dtype=np.uint16)
+    k = np.zeros_like(q)
+    v = np.zeros_like(q)
+    parts = [p for p in parts if p[0].shape[1] > 0]
+    for (start, rows, _), (pq, pk, pv) in zip(segs, parts):
+        q[0, :, start:start + rows] = pq
+        k[0, :, start:start + rows] = pk
+        v[0, :, start:start + rows] = pv
+    end = segs[-1][0] + segs[-1][1]
+    return Workload("ref2va_segments", 1, H, L, L, d, end, end, q, k, v, threshold=threshold,
+                    centroids_per_block=centroids_per_block, kblock=kblock, k_scale_rows=kblock,
+                    segments=np.array(segs, dtype=np.int32))
 
 
 CONFIG_NAMES = {
