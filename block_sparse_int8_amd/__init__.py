@@ -22,7 +22,7 @@ from typing import Optional, Sequence
 
 import torch
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 SA_OK, SA_E_NULL, SA_E_SHAPE, SA_E_ALIGN, SA_E_VALUE, SA_E_UNSUPPORTED, SA_E_DEVICE, SA_E_LAUNCH, SA_E_WORKSPACE = range(9)
 SA_DROP, SA_EXACT, SA_CENTROID = 0, 1, 2
 SA_BF16, SA_INT8, SA_F32 = 0, 1, 2
@@ -43,10 +43,16 @@ class sa_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "H", "Lq", "Lkv", "d", "lq_valid", "lkv_valid", "Lv")]
 
 
+class sa_segment(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("start", "rows", "routed")]
+
+
 class sa_route_params(ctypes.Structure):
     _fields_ = [("threshold", ctypes.c_float)] + [
         (n, ctypes.c_int32) for n in ("centroids_per_block", "prefix_tokens", "kblock", "k_scale_rows",
-                                      "v_scale_rows", "map_kblock", "rule")] + [("sparsity", ctypes.c_float)]
+                                      "v_scale_rows", "map_kblock", "rule")] + [
+        ("sparsity", ctypes.c_float), ("n_segments", ctypes.c_int32),
+        ("segments_host", ctypes.POINTER(sa_segment))]
 
 
 def search_paths():
@@ -158,9 +164,15 @@ def _dims(B, H, Lq, Lkv, d, lq_valid, lkv_valid, Lv):
 
 
 def _params(threshold, G, prefix, kblock, k_scale_rows, v_scale_rows, map_kblock, rule=SA_RULE_THRESHOLD,
-            sparsity=0.0):
-    return sa_route_params(float(threshold), G, prefix, kblock, k_scale_rows, v_scale_rows, map_kblock, int(rule),
-                           float(sparsity))
+            sparsity=0.0, segments=None):
+    """The parameter struct; ``segments`` is a sequence of (start, rows, routed).
+    The struct keeps a reference to its segment array."""
+    segs = [] if segments is None else [tuple(int(x) for x in g) for g in segments]
+    arr = (sa_segment * max(1, len(segs)))(*[sa_segment(*g) for g in segs])
+    prm = sa_route_params(float(threshold), G, prefix, kblock, k_scale_rows, v_scale_rows, map_kblock, int(rule),
+                          float(sparsity), len(segs), ctypes.cast(arr, ctypes.POINTER(sa_segment)) if segs else None)
+    prm._segments_keepalive = arr
+    return prm
 
 
 def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor, v: torch.Tensor, *,
@@ -169,12 +181,14 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
                       threshold: float = 1.0, centroids_per_block: int = 1, prefix_tokens: int = 0,
                       kblock: int = 64, k_scale_rows: Optional[int] = None, v_scale_rows: int = 128,
                       explicit_map: Optional[torch.Tensor] = None, map_kblock: Optional[int] = None,
-                      rule: int = SA_RULE_THRESHOLD, sparsity: float = 0.0,
+                      rule: int = SA_RULE_THRESHOLD, sparsity: float = 0.0, segments=None,
                       row_stats: bool = False, workspace: Optional[torch.Tensor] = None,
                       outputs: Optional[dict] = None, stream=None) -> dict:
     """Block map + centroids.  ``rule`` picks the threshold rule (``threshold``)
-    or the fixed-sparsity rule (``sparsity``).  Returns dict(map, k_centroid,
-    v_centroid, count, row_stats) with the shapes of sparse_attn.h."""
+    or the fixed-sparsity rule (``sparsity``); ``segments`` ((start, rows,
+    routed) triples) gives a segmented key layout in place of the prefix.
+    Returns dict(map, k_centroid, v_centroid, count, row_stats) with the shapes
+    of sparse_attn.h."""
     B, H, Lq, d = q8.shape
     Lkv = k8.shape[2]
     Lv = v.shape[2]
@@ -196,7 +210,8 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
     if explicit_map is not None:
         _need(explicit_map, "explicit_map", torch.uint8, (B, H, nQB, Lkv // map_kblock))
     dims = _dims(B, H, Lq, Lkv, d, lq_valid, lkv_valid, Lv)
-    prm = _params(threshold, G, prefix_tokens, kblock, k_scale_rows, v_scale_rows, map_kblock, rule, sparsity)
+    prm = _params(threshold, G, prefix_tokens, kblock, k_scale_rows, v_scale_rows, map_kblock, rule, sparsity,
+                  segments)
     lib = load()
     outputs = {} if outputs is None else outputs
     dev = q8.device
@@ -237,8 +252,10 @@ def sparse_attn_fwd(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k
                     centroids_per_block: int = 1, kblock: int = 64, k_scale_rows: Optional[int] = None,
                     v_scale_rows: int = 128, sm_scale: Optional[float] = None,
                     out_dtype: torch.dtype = torch.float32, return_lse: bool = False,
-                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
-    """Attention output [B,H,Lq,d] (and lse [B,H,Lq] when asked)."""
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, segments=None,
+                    stream=None):
+    """Attention output [B,H,Lq,d] (and lse [B,H,Lq] when asked).  ``segments``
+    must be the key layout the map was routed with."""
     B, H, Lq, d = q8.shape
     Lkv = k8.shape[2]
     Lv = v.shape[2]
@@ -272,7 +289,7 @@ def sparse_attn_fwd(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k
         _need(lse, "lse", torch.float32, (B, H, Lq))
     sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
     dims = _dims(B, H, Lq, Lkv, d, lq_valid, lkv_valid, Lv)
-    prm = _params(float("nan"), G, 0, kblock, k_scale_rows, v_scale_rows, kblock)
+    prm = _params(float("nan"), G, 0, kblock, k_scale_rows, v_scale_rows, kblock, segments=segments)
     _check(load().sparse_attn_fwd(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), v_dtype, _ptr(v_scale),
                                   _ptr(v_block_src), ctypes.byref(dims), ctypes.byref(prm), _ptr(block_map),
                                   _ptr(k_centroid), _ptr(v_centroid), _ptr(count), float(sm), _ptr(out), odt,
@@ -306,7 +323,8 @@ def gather_virtual_kv(k_phys: torch.Tensor, rows_per_slice: int, src_map: Sequen
 def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, lq_valid=None, lkv_valid=None,
                      threshold: float = 1.0, centroids_per_block: int = 1, prefix_tokens: int = 0,
                      explicit_map: Optional[torch.Tensor] = None, map_kblock: Optional[int] = None,
-                     rule: int = SA_RULE_THRESHOLD, sparsity: float = 0.0, kblock: int = 64, sm_scale: Optional[float] = None, out_dtype=torch.float32,
+                     rule: int = SA_RULE_THRESHOLD, sparsity: float = 0.0, segments=None, kblock: int = 64,
+                     sm_scale: Optional[float] = None, out_dtype=torch.float32,
                      return_lse: bool = False, stream=None):
     """quantize_qk_int8(Q, 128 rows) -> quantize_qk_int8(K, kblock rows) ->
     sparse_attn_route -> sparse_attn_fwd, all on one stream.  q, k, v are bf16
@@ -319,9 +337,9 @@ def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, lq_va
     r = sparse_attn_route(q8, k8, ks, v, lq_valid=lq_valid, lkv_valid=lkv_valid, threshold=threshold,
                           centroids_per_block=centroids_per_block, prefix_tokens=prefix_tokens, kblock=kblock,
                           explicit_map=explicit_map, map_kblock=map_kblock, rule=rule, sparsity=sparsity,
-                          stream=stream)
+                          segments=segments, stream=stream)
     res = sparse_attn_fwd(q8, qs, k8, ks, v, r["map"], k_centroid=r["k_centroid"], v_centroid=r["v_centroid"],
                           count=r["count"], lq_valid=lq_valid, lkv_valid=lkv_valid,
                           centroids_per_block=centroids_per_block, kblock=kblock, sm_scale=sm_scale,
-                          out_dtype=out_dtype, return_lse=return_lse, stream=stream)
+                          out_dtype=out_dtype, return_lse=return_lse, segments=segments, stream=stream)
     return res, r["map"]

@@ -103,6 +103,41 @@ int32_t check_dims(const sa_dims* dm, const sa_route_params* p, bool has_vbs) {
   return SA_OK;
 }
 
+// Key layout from the segment list, or from the prefix and the valid length.
+int32_t build_layout(const sa_dims* dm, const sa_route_params* p, sa::KvLayout* lay) {
+  *lay = sa::KvLayout{};
+  lay->kblock = p->kblock;
+  if (p->n_segments == 0) {
+    lay->n = 2;
+    lay->start[0] = 0;
+    lay->end[0] = p->prefix_tokens < dm->lkv_valid ? p->prefix_tokens : dm->lkv_valid;
+    lay->start[1] = p->prefix_tokens;
+    lay->end[1] = dm->lkv_valid;
+    lay->routed = 2u;
+    return SA_OK;
+  }
+  if (p->n_segments < 0 || p->n_segments > SA_MAX_SEGMENTS)
+    return fail(SA_E_VALUE, "n_segments must be in [0, %d] (got %d)", SA_MAX_SEGMENTS, p->n_segments);
+  if (!p->segments_host) return fail(SA_E_NULL, "segments_host is required when n_segments > 0");
+  if (p->prefix_tokens != 0) return fail(SA_E_VALUE, "prefix_tokens must be 0 when segments are given");
+  int prev_end = 0;
+  for (int x = 0; x < p->n_segments; ++x) {
+    const sa_segment& g = p->segments_host[x];
+    if (g.start < 0 || g.start % p->kblock)
+      return fail(SA_E_VALUE, "segment %d: start %d is not a non-negative multiple of kblock", x, g.start);
+    if (g.rows < 0 || g.start + g.rows > dm->lkv_valid)
+      return fail(SA_E_VALUE, "segment %d: rows %d outside [0, lkv_valid - start]", x, g.rows);
+    if (x > 0 && g.start < prev_end)
+      return fail(SA_E_VALUE, "segment %d starts at %d, inside the previous segment", x, g.start);
+    prev_end = g.start + g.rows;
+    lay->start[x] = g.start;
+    lay->end[x] = g.start + g.rows;
+    if (g.routed) lay->routed |= 1u << x;
+  }
+  lay->n = p->n_segments;
+  return SA_OK;
+}
+
 int32_t check_v(int32_t v_dtype, const void* v, const float* v_scale, const sa_dims* dm, const sa_route_params* p) {
   if (v_dtype != SA_BF16 && v_dtype != SA_INT8) return fail(SA_E_VALUE, "v_dtype must be SA_BF16 or SA_INT8");
   if (!v) return fail(SA_E_NULL, "v must not be NULL");
@@ -160,6 +195,8 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
                           float* k_centroid, float* v_centroid, float* count, double* row_stats, void* workspace,
                           size_t workspace_bytes, void* stream) {
   if (const int32_t rc = check_dims(dims, p, v_block_src != nullptr)) return rc;
+  sa::KvLayout lay;
+  if (const int32_t rc = build_layout(dims, p, &lay)) return rc;
   if (!q || !k || !k_scale || !block_map) return fail(SA_E_NULL, "sparse_attn_route: q, k, k_scale and block_map are required");
   if (!aligned16(q) || !aligned16(k)) return fail(SA_E_ALIGN, "sparse_attn_route: q and k must be 16-byte aligned");
   const int G = p->centroids_per_block;
@@ -197,6 +234,7 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
   if (const int32_t rc = check_current_device()) return rc;
   if (dims->Lq == 0 || dims->Lkv == 0) return ok();
   sa::RouteArgs a{};
+  a.lay = lay;
   a.q = q; a.k = k; a.k_scale = k_scale; a.v = v; a.v_int8 = v_dtype == SA_INT8; a.v_scale = v_scale;
   a.v_block_src = v_block_src;
   a.B = dims->B; a.H = dims->H; a.Lq = dims->Lq; a.Lkv = dims->Lkv; a.Lv = dims->Lv; a.d = dims->d;
@@ -222,6 +260,8 @@ int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k, 
                         const float* v_centroid, const float* count, float sm_scale, void* out, int32_t out_dtype,
                         float* lse, void* stream) {
   if (const int32_t rc = check_dims(dims, p, v_block_src != nullptr)) return rc;
+  sa::KvLayout lay;
+  if (const int32_t rc = build_layout(dims, p, &lay)) return rc;
   if (!q || !q_scale || !k || !k_scale || !block_map || !out)
     return fail(SA_E_NULL, "sparse_attn_fwd: q, q_scale, k, k_scale, block_map and out are required");
   if (!aligned16(q) || !aligned16(k) || !aligned16(out)) return fail(SA_E_ALIGN, "sparse_attn_fwd: q, k and out must be 16-byte aligned");
@@ -236,6 +276,7 @@ int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k, 
   if (const int32_t rc = check_current_device()) return rc;
   if (dims->Lq == 0) return ok();
   sa::FwdArgs a{};
+  a.lay = lay;
   a.q = q; a.q_scale = q_scale; a.k = k; a.k_scale = k_scale; a.v = v; a.v_scale = v_scale; a.v_block_src = v_block_src;
   a.map = block_map; a.kc = k_centroid; a.vc = v_centroid; a.cnt = count; a.out = out; a.lse = lse;
   a.B = dims->B; a.H = dims->H; a.Lq = dims->Lq; a.Lkv = dims->Lkv; a.Lv = dims->Lv; a.d = dims->d;

@@ -476,6 +476,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t stage1[L::STAGE];
   __shared__ uint16_t elist[2 * kWin];
   __shared__ uint16_t clist[kWin];
+  __shared__ int plist[kMaxSegments], pvalid[kMaxSegments];
   __shared__ float bias[32];
   __shared__ int cnts[3];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -532,45 +533,43 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const int wend = min(a.nKB, w0 + kWin);
     __syncthreads();
     if (wave == 0) {
-      // Exact tiles go to elist, except the one tile that holds the end of the
-      // valid keys (it needs masking and is done after the pipelined loop);
-      // tiles entirely past the valid keys are skipped.
-      int nE = 0, nC = 0, ptile = -1;
+      // Full exact tiles go to elist.  A tile holding the end of a segment's
+      // valid keys (the valid keys of a block are a prefix of it) goes to
+      // plist with its valid count: it needs masking and is done after the
+      // pipelined loop.  Tiles without valid keys are skipped.
+      int nE = 0, nC = 0, nP = 0;
       const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       for (int c0 = w0; c0 < wend; c0 += 64) {
         const int j = c0 + lane;
         const int st = j < wend ? mrow[j] : 0;
         const bool isE = st == 1, isC = st == 2 && a.G > 0;
-        int nf = 0;
-        if (isE) {
-          for (int sub = 0; sub < tpb; ++sub) {
-            const int tr0 = (j * tpb + sub) * kTile;
-            if (tr0 + kTile <= a.lkv_valid) ++nf;
-            else if (tr0 < a.lkv_valid) ptile = j * tpb + sub;
-          }
-        }
-        const uint64_t b0 = __ballot(nf & 1), b1 = __ballot(nf & 2), bC = __ballot(isC);
+        const int nv = isE ? a.lay.block_rows(j) : 0;
+        const int nf = nv / kTile, pv = nv % kTile;   // full tiles, valid keys of the partial one
+        const uint64_t b0 = __ballot(nf & 1), b1 = __ballot(nf & 2), bC = __ballot(isC), bP = __ballot(pv > 0);
         if (nf) {
-          int pos = nE + __popcll(b0 & lt) + 2 * __popcll(b1 & lt);
-          for (int sub = 0; sub < tpb; ++sub) {
-            const int tr0 = (j * tpb + sub) * kTile;
-            if (tr0 + kTile <= a.lkv_valid) elist[pos++] = (uint16_t)((j - w0) * tpb + sub);
+          const int pos = nE + __popcll(b0 & lt) + 2 * __popcll(b1 & lt);
+          for (int sub = 0; sub < nf; ++sub) elist[pos + sub] = (uint16_t)((j - w0) * tpb + sub);
+        }
+        if (pv > 0) {
+          const int pos = nP + __popcll(bP & lt);
+          if (pos < kMaxSegments) {
+            plist[pos] = j * tpb + nf;
+            pvalid[pos] = pv;
           }
         }
         if (isC) clist[nC + __popcll(bC & lt)] = (uint16_t)(j - w0);
         nE += __popcll(b0) + 2 * __popcll(b1);
         nC += __popcll(bC);
+        nP += __popcll(bP);
       }
-      const uint64_t bp = __ballot(ptile >= 0);
       if (lane == 0) {
         cnts[0] = nE;
         cnts[1] = nC;
-        cnts[2] = -1;
+        cnts[2] = min(nP, kMaxSegments);
       }
-      if (bp && lane == __builtin_ctzll(bp)) cnts[2] = ptile;
     }
     __syncthreads();
-    const int nE = cnts[0], nC = cnts[1], ptile = cnts[2];
+    const int nE = cnts[0], nC = cnts[1], nP = cnts[2];
 
     // ---------------- exact 64-key tiles, two-stage pipeline ----------------
     if (nE > 0) {
@@ -603,13 +602,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       }
     }
     __syncthreads();                             // stages free again
-    if (ptile >= 0) {                            // the tile with the end of the valid keys
-      const TileInfo t = fetch_tile<VI8>(a, bh, ptile, nKS, nVS);
+    for (int pi = 0; pi < nP; ++pi) {            // tiles with the end of a segment's valid keys
+      const TileInfo t = fetch_tile<VI8>(a, bh, plist[pi], nKS, nVS);
+      const int nvalid = pvalid[pi];
       if (VI8) load_v_int8<D>(v8base + (int64_t)t.vrow0 * D, vr, tid);
       tile_copy<D, VI8>(t, stage0, krs, vrs, plan, wave, true).all();
       if (VI8) store_v_int8<D>(stage0, vr, tid);
       __syncthreads();
-      exact_tile<D, VI8, true>(stage0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, a.lkv_valid - t.krow0,
+      exact_tile<D, VI8, true>(stage0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, nvalid,
                                klane, vlane, hh, tile_copy<D, VI8>(t, stage1, krs, vrs, plan, wave, false));
       __syncthreads();
     }

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
   const int64_t bh = (int64_t)b * a.H + h;
   const int kb = MAXCH * 32, row0 = j * kb, nch = MAXCH;
   const int nKS = a.Lkv / a.k_scale_rows;
-  const int nvalid = min(kb, max(0, a.lkv_valid - row0));
+  const int nvalid = a.lay.block_rows(j);   // valid rows: a prefix of the block
   // K: lane (dw, rg) sums rows rg, rg + KRG, ... of each chunk
   {
     constexpr int NR = 32 / KRG;
@@ -265,7 +265,8 @@ struct ProxyTiles {
       p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ql[s], k.h[s], p2, 0, 0, 0);
       p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ql[s], k.l[s], p3, 0, 0, 0);
     }
-    const double w = j < a.nKB ? (double)a.k_scale[bh * nKS + j] / (double)min(kb, a.lkv_valid - j * kb) : 0.0;
+    const int nj = j < a.nKB ? a.lay.block_rows(j) : 0;
+    const double w = nj > 0 ? (double)a.k_scale[bh * nKS + j] / (double)nj : 0.0;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       sv[e] = (16384.0 * (double)p1[e] + 128.0 * (double)p2[e] + (double)p3[e]) * w;
@@ -289,16 +290,33 @@ struct DecideItem {
   }
 };
 
-// Routing candidates form the contiguous key-block range [jc0, jc1): blocks
-// with a valid row at or after the protected prefix.
+// Class of key block j in the key layout: 0 without valid rows (dropped),
+// 1 dense (always exact), 2 a routing candidate.
+__host__ __device__ __forceinline__ int block_class(const KvLayout& lay, int j) {
+  if (lay.block_rows(j) == 0) return 0;
+  return lay.block_routed(j) ? 2 : 1;
+}
+
+// Routing candidates: the key blocks with a valid row in routed segments.  They
+// lie in [jc0, jc1) (N of them; the range may hold other blocks between
+// routed segments).
 struct CandRange {
   int jc0, jc1, N;
-  __device__ __forceinline__ explicit CandRange(const RouteArgs& a) {
-    jc0 = (a.prefix + a.kblock - 1) / a.kblock;
-    jc1 = min(a.nKB, (a.lkv_valid + a.kblock - 1) / a.kblock);
-    N = max(0, jc1 - jc0);
+  const KvLayout* lay;
+  __host__ __device__ __forceinline__ explicit CandRange(const RouteArgs& a) : jc0(0), jc1(0), N(0), lay(&a.lay) {
+    const int kb = a.lay.kblock;
+    bool any = false;
+    for (int x = 0; x < a.lay.n; ++x) {
+      if (!((a.lay.routed >> x) & 1u) || a.lay.end[x] <= a.lay.start[x]) continue;
+      const int b0 = a.lay.start[x] / kb, b1 = min(a.nKB, (a.lay.end[x] + kb - 1) / kb);
+      if (b1 <= b0) continue;
+      jc0 = any ? min(jc0, b0) : b0;
+      jc1 = any ? max(jc1, b1) : b1;
+      N += b1 - b0;
+      any = true;
+    }
   }
-  __device__ __forceinline__ bool has(int j) const { return j >= jc0 && j < jc1; }
+  __device__ __forceinline__ bool has(int j) const { return j >= jc0 && j < jc1 && block_class(*lay, j) == 2; }
 };
 
 // Sol decisions (threshold rule) for 32 query blocks of one (head, batch): three
@@ -388,14 +406,12 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_sol_kernel(RouteArgs
       pt.load_k(a, tt, kc);
       pt.tile(a, tt, kc, sv);
     }
+    const int cls = j < a.nKB ? block_class(a.lay, j) : 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = pt.row_of(e), i = i0 + r;
       if (i >= a.nQB || j >= a.nKB) continue;
-      uint8_t st;
-      if (j * a.kblock >= a.lkv_valid) st = 0;
-      else if (j * a.kblock < a.prefix) st = 1;
-      else st = (!keep_s[r] && sv[e] > thr_s[r]) ? 2 : 1;
+      const uint8_t st = cls < 2 ? (uint8_t)cls : ((!keep_s[r] && sv[e] > thr_s[r]) ? 2 : 1);
       a.map[(bh * a.nQB + i) * a.nKB + j] = st;
     }
   }
@@ -547,13 +563,13 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_topk_kernel(RouteArg
       pt.tile(a, tt, kc, sv);
     }
     const uint32_t lo = ~(uint32_t)j;
+    const int cls = j < a.nKB ? block_class(a.lay, j) : 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = pt.row_of(e), i = i0 + r;
       if (i >= a.nQB || j >= a.nKB) continue;
       uint8_t st;
-      if (j * a.kblock >= a.lkv_valid) st = 0;
-      else if (j * a.kblock < a.prefix) st = 1;
+      if (cls < 2) st = (uint8_t)cls;
       else if (!select) st = keep > 0 ? 1 : pruned;
       else {
         const int pd = dig_s[r];
@@ -571,7 +587,8 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_topk_kernel(RouteArg
 // Decisions with the proxies held in LDS.  When a query block has at most
 // kLdsCand candidates, one pass of matrix-core tiles writes s_ij for the 32
 // query blocks of a workgroup into a 32 x kLdsCand float64 array (128 KiB),
-// and every later pass reads it from there.  The rules and their arithmetic are
+// and every later pass reads it from there (slot j - jc0; NaN for blocks in
+// that range that are not candidates).  The rules and their arithmetic are
 // those of the kernels above; only where s lives changes (and the summation
 // order of the mean and variance).  One workgroup per CU; kLdsWaves waves.
 // ---------------------------------------------------------------------------
@@ -590,27 +607,24 @@ __device__ __forceinline__ void proxies_to_lds(const RouteArgs& a, const ProxyTi
     double sv[16];
     pt.tile(a, tt, kc, sv);
     const int j = tt * 32 + pt.n;
-    if (!cr.has(j)) continue;
+    if (j < cr.jc0 || j >= cr.jc1) continue;
+    const bool cand = cr.has(j);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sv_s[pt.row_of(e)][j - cr.jc0] = sv[e];
+    for (int e = 0; e < 16; ++e) sv_s[pt.row_of(e)][j - cr.jc0] = cand ? sv[e] : __builtin_nan("");
   }
 }
 
-// Block states of query block i0 + r for every key block, one coalesced row of
-// bytes at a time: DROP past the valid keys, EXACT in the prefix, cand_state(c)
-// for candidate c.
+// Block states of the workgroup's query blocks: DROP for key blocks without
+// valid rows, EXACT for dense ones, cand_state(r, j - jc0) for candidates.  A
+// thread owns key blocks j, j + nt, ...; each store covers consecutive blocks
+// of one row.
 template <typename F>
 __device__ __forceinline__ void write_map_rows(const RouteArgs& a, int64_t bh, int i0, const CandRange& cr, int nt,
                                                F cand_state) {
-  for (int r = 0; r < 32 && i0 + r < a.nQB; ++r) {
-    uint8_t* mrow = a.map + (bh * a.nQB + i0 + r) * a.nKB;
-    for (int j = threadIdx.x; j < a.nKB; j += nt) {
-      uint8_t st;
-      if (j * a.kblock >= a.lkv_valid) st = 0;
-      else if (j * a.kblock < a.prefix) st = 1;
-      else st = cand_state(r, j - cr.jc0);
-      mrow[j] = st;
-    }
+  for (int j = threadIdx.x; j < a.nKB; j += nt) {
+    const int cls = block_class(a.lay, j);
+    for (int r = 0; r < 32 && i0 + r < a.nQB; ++r)
+      a.map[(bh * a.nQB + i0 + r) * a.nKB + j] = cls < 2 ? (uint8_t)cls : cand_state(r, j - cr.jc0);
   }
 }
 
@@ -630,16 +644,20 @@ __global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
   proxies_to_lds<D, NW>(a, pt, cr, wave, sv_s);
   __syncthreads();
   // row r's mean and population variance: TPR adjacent lanes per row
-  const int r = t / TPR, part = t % TPR;
+  const int r = t / TPR, part = t % TPR, span = cr.jc1 - cr.jc0;
   double acc = 0.0;
-  for (int c = part; c < N; c += TPR) acc += sv_s[r][c];
+  for (int c = part; c < span; c += TPR) {
+    const double v = sv_s[r][c];
+    acc += __builtin_isnan(v) ? 0.0 : v;
+  }
 #pragma unroll
   for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
   const double mu = N > 0 ? acc / N : __builtin_nan("");
   double acc2 = 0.0;
-  for (int c = part; c < N; c += TPR) {
-    const double dl = sv_s[r][c] - mu;
-    acc2 += dl * dl;
+  for (int c = part; c < span; c += TPR) {
+    const double v = sv_s[r][c];
+    const double dl = v - mu;
+    acc2 += __builtin_isnan(v) ? 0.0 : dl * dl;
   }
 #pragma unroll
   for (int o = TPR / 2; o >= 1; o >>= 1) acc2 += __shfl_xor(acc2, o, 64);
@@ -681,7 +699,7 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
   const int64_t bh = (int64_t)wi.b * a.H + wi.h;
   const int i0 = wi.i0;
   const CandRange cr(a);
-  const int N = cr.N;
+  const int N = cr.N, span = cr.jc1 - cr.jc0;
   const int keep = N - (int)floor((double)a.sparsity * (double)N);
   const uint8_t pruned = a.G > 0 ? 2 : 0;
   const bool select = keep > 0 && keep < N;
@@ -702,11 +720,13 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int c = lane + 64 * k;
-        const uint64_t hk = c < N ? order_key(sv_s[r][c]) : 0ull;
+        const double v = c < span ? sv_s[r][c] : __builtin_nan("");
+        const bool cand = !__builtin_isnan(v);
+        const uint64_t hk = cand ? order_key(v) : 0ull;
         w0[k] = (uint32_t)(hk >> 32);
         w1[k] = (uint32_t)hk;
         w2[k] = ~(uint32_t)(cr.jc0 + c);
-        live[k] = __ballot(c < N);
+        live[k] = __ballot(cand);
       }
       int m = N, rem = keep, nb = 0;
       uint64_t ph = 0;
@@ -772,8 +792,9 @@ __global__ __launch_bounds__(256) void decide_explicit_kernel(RouteArgs a) {
   for (int j = t; j < a.nKB; j += 256) {
     int st = erow[(int64_t)j * a.kblock / a.map_kblock];
     if (st > 2 || (st == 2 && a.G == 0)) st = 1;
-    if (j * a.kblock < a.prefix) st = 1;
-    if (j * a.kblock >= a.lkv_valid) st = 0;
+    const int cls = block_class(a.lay, j);
+    if (cls == 1) st = 1;
+    if (cls == 0) st = 0;
     mrow[j] = (uint8_t)st;
   }
   if (a.stats && t == 0) {
@@ -805,9 +826,8 @@ static hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
   }
   if (sol) {
     const dim3 grid((a.nQB + 31) / 32 * a.H * a.B);
-    const int jc0 = (a.prefix + a.kblock - 1) / a.kblock;
-    const int jc1 = min(a.nKB, (a.lkv_valid + a.kblock - 1) / a.kblock);
-    const bool lds = jc1 - jc0 <= kLdsCand;   // candidates' proxies fit in LDS
+    const CandRange cr(a);
+    const bool lds = cr.jc1 - cr.jc0 <= kLdsCand;   // candidates' proxies fit in LDS
     if (a.rule == kRuleTopK) {
       if (lds) decide_topk_lds_kernel<D, kLdsWaves><<<grid, 64 * kLdsWaves, 0, st>>>(a);
       else decide_topk_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);

@@ -16,6 +16,39 @@ struct SrcMap {
   int32_t v[kMaxLogical];
 };
 
+// Key layout: up to kMaxSegments segments in increasing start, each starting on
+// a key-block boundary; valid key rows are [start, end) of a segment (end
+// already capped at the valid length).  A key block lies in at most one
+// segment, and its valid rows are a prefix of the block.  The plain layout
+// (a dense prefix, then routed rows up to the valid length) is two segments.
+constexpr int kMaxSegments = 16;
+
+struct KvLayout {
+  int n;
+  int start[kMaxSegments];
+  int end[kMaxSegments];
+  uint32_t routed;   // bit s set: segment s is routed
+  int kblock;
+
+  // segment holding row r (the last starting at or before it), or -1
+  __host__ __device__ int seg_of(int r) const {
+    int s = -1;
+    for (int x = 0; x < n; ++x) s = start[x] <= r ? x : s;
+    return s;
+  }
+  // valid rows of key block j (a prefix of the block)
+  __host__ __device__ int block_rows(int j) const {
+    const int r0 = j * kblock, s = seg_of(r0);
+    if (s < 0) return 0;
+    const int v = end[s] - r0;
+    return v < 0 ? 0 : (v > kblock ? kblock : v);
+  }
+  __host__ __device__ bool block_routed(int j) const {
+    const int s = seg_of(j * kblock);
+    return s >= 0 && ((routed >> s) & 1u);
+  }
+};
+
 struct QuantizeArgs {
   const uint16_t* x;
   int64_t sB, sH, sL;
@@ -45,6 +78,7 @@ struct RouteArgs {
   const int32_t* v_block_src;
   int B, H, Lq, Lkv, Lv, d, lq_valid, lkv_valid;
   int nQB, nKB, kblock, G, prefix, k_scale_rows, v_scale_rows, map_kblock;
+  KvLayout lay;
   int rule;        // kRuleThreshold or kRuleTopK (routing rules without an explicit map)
   float tau;       // threshold rule
   float sparsity;  // fixed-sparsity rule: fraction of candidates pruned
@@ -74,6 +108,7 @@ struct FwdArgs {
   float* lse;
   int B, H, Lq, Lkv, Lv, d, lq_valid, lkv_valid;
   int nQB, nKB, kblock, G, k_scale_rows, v_scale_rows;
+  KvLayout lay;
   bool v_int8, out_bf16;
   float sm_log2;   // sm_scale * log2(e)
 };

@@ -34,6 +34,12 @@
  *    lq_valid / lkv_valid (rows at or past them are padding: excluded from
  *    scales, sums, centroids and softmax; padded output rows are written as 0
  *    with lse = -inf).
+ *  - A segmented key layout (sa_segment) also pads each segment to a key-block
+ *    boundary.  Route and forward exclude those rows from counts, centroids and
+ *    the softmax; quantize_qk_int8 does not know the layout, so padding rows
+ *    should hold zeros (they then code to 0 and leave a block's scale as it
+ *    would be without them).  Query rows inside the layout's padding are
+ *    computed like any other row below lq_valid.
  *  - Only gfx950 devices are accepted; others give SA_E_UNSUPPORTED.
  */
 #ifndef SPARSE_ATTN_H
@@ -46,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 2
+#define SA_ABI_VERSION 3
 
 enum sa_status {
   SA_OK = 0,
@@ -81,6 +87,22 @@ typedef struct sa_dims {
                                   v_block_src remaps 64-row V blocks (virtual KV) */
 } sa_dims;
 
+/* One segment of the key sequence (Ref2VA VSA, two-stage attention patch:
+ * text, reference-image and reference-audio tokens get key tiles of their own
+ * that stay dense, and only generated-video key tiles are pruned; Configure
+ * Sol Sparse Attention, "The inputs that matter": a reference video may be
+ * routed as well, and the auto prefix policy follows the model's layout). */
+typedef struct sa_segment {
+  int32_t start;               /* first key row: a multiple of kblock, so that no key
+                                  block spans two segments */
+  int32_t rows;                /* valid rows (>= 0); rows from start + rows up to the
+                                  next segment's start are padding */
+  int32_t routed;              /* nonzero: its key blocks are routing candidates;
+                                  zero: dense (always SA_EXACT) */
+} sa_segment;
+
+#define SA_MAX_SEGMENTS 16
+
 typedef struct sa_route_params {
   float threshold;             /* routing_threshold tau (Sol rule); +inf keeps every block
                                   exact, -inf makes every candidate a centroid; NaN is
@@ -96,6 +118,12 @@ typedef struct sa_route_params {
   int32_t rule;                /* SA_RULE_THRESHOLD or SA_RULE_TOPK (ignored with an explicit map) */
   float sparsity;              /* SA_RULE_TOPK: fraction of the candidates pruned per query
                                   block, in [0, 1]; NaN or outside is rejected */
+  int32_t n_segments;          /* 0: the key layout is the prefix (dense) then routed rows
+                                  up to lkv_valid; 1..SA_MAX_SEGMENTS: segments_host
+                                  describes it (prefix_tokens must then be 0) */
+  const sa_segment* segments_host; /* host array of n_segments, in increasing start,
+                                  non-overlapping, start + rows <= lkv_valid; read during
+                                  the call only */
 } sa_route_params;
 
 /* ABI version of this build (SA_ABI_VERSION).  A caller compiled against another
@@ -146,8 +174,8 @@ size_t sparse_attn_route_workspace_size(const sa_dims* dims, const sa_route_para
  *   explicit_map NULL: Sol rule.  Else uint8 [B,H,Lq/128,Lkv/map_kblock]; values
  *             above 2, and centroid entries when G = 0, are taken as SA_EXACT.
  *   block_map out uint8 [B,H,Lq/128,Lkv/kblock]:
- *             Candidates are key blocks with a valid row at or after the
- *             prefix; proxy s_ij = (sum of INT8 Q codes of query block i) .
+ *             Candidates are routed key blocks with a valid row: at or after
+ *             the prefix, or in a routed segment; proxy s_ij = (sum of INT8 Q codes of query block i) .
  *             (sum of INT8 K codes of key block j) * b_j / n_j (n_j valid rows,
  *             b_j the block's K scale) — the dot of the dequantized block means
  *             up to a positive per-query-block factor, exact in float64.
@@ -160,8 +188,8 @@ size_t sparse_attn_route_workspace_size(const sa_dims* dims, const sa_route_para
  *             candidates, the N - floor(sparsity * N) of largest s_ij (the
  *             product in float64; equal s_ij ordered by lower block index) are
  *             SA_EXACT, the others SA_CENTROID when G > 0 and SA_DROP when G = 0.
- *             Prefix blocks SA_EXACT; key blocks without valid rows SA_DROP
- *             (also for maps).
+ *             Prefix blocks and blocks of dense segments SA_EXACT; key blocks
+ *             without valid rows SA_DROP (also for maps).
  *   k_centroid, v_centroid out fp32 [B,H,Lkv/kblock,G,d]; count out fp32
  *             [B,H,Lkv/kblock,G]: group g covers rows [g*kblock/G,(g+1)*kblock/G)
  *             of the block; kbar = mean of the dequantized INT8 keys, vbar =
@@ -193,6 +221,9 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
  * MFMA with fp32 accumulation); kbar/vbar enter as bf16 hi+lo pairs.
  *   q, q_scale  int8 [B,H,Lq,d], fp32 [B,H,Lq/128]
  *   k, k_scale, v, v_dtype, v_scale, v_block_src: as for sparse_attn_route
+ *   p           kblock, k_scale_rows, v_scale_rows, centroids_per_block and the
+ *               key layout (segments, lkv_valid) are used; the routing fields
+ *               are ignored
  *   block_map   uint8 [B,H,Lq/128,Lkv/kblock] (values > 2 are taken as SA_DROP)
  *   k_centroid, v_centroid, count: route outputs (may be NULL when G = 0)
  *   out         [B,H,Lq,d] fp32 (SA_F32) or bf16 (SA_BF16)

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 2
+    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 3
 
 
 def test_missing_library_lists_search_paths(monkeypatch, tmp_path):
@@ -90,11 +90,11 @@ def _dims(**kw):
 
 def _prm(**kw):
     d = dict(threshold=1.0, centroids_per_block=1, prefix_tokens=0, kblock=64, k_scale_rows=64, v_scale_rows=128,
-             map_kblock=64, rule=sa.SA_RULE_THRESHOLD, sparsity=0.0)
+             map_kblock=64, rule=sa.SA_RULE_THRESHOLD, sparsity=0.0, segments=None)
     d.update(kw)
-    return sa.sa_route_params(d["threshold"], *[d[k] for k in ("centroids_per_block", "prefix_tokens", "kblock",
-                                                                   "k_scale_rows", "v_scale_rows", "map_kblock",
-                                                                   "rule", "sparsity")])
+    return sa._params(d["threshold"], *[d[k] for k in ("centroids_per_block", "prefix_tokens", "kblock",
+                                                           "k_scale_rows", "v_scale_rows", "map_kblock",
+                                                           "rule", "sparsity", "segments")])
 
 
 def _route(dims, prm, em=None, ws=None, wsb=0, G_out=True):
@@ -121,6 +121,11 @@ def _route(dims, prm, em=None, ws=None, wsb=0, G_out=True):
     ({}, dict(rule=sa.SA_RULE_TOPK, sparsity=-0.25), sa.SA_E_VALUE, "sparsity"),
     ({}, dict(rule=sa.SA_RULE_TOPK, sparsity=float("nan")), sa.SA_E_VALUE, "sparsity"),
     ({}, dict(rule=sa.SA_RULE_TOPK, sparsity=0.5, k_scale_rows=128), sa.SA_E_VALUE, "k_scale_rows == kblock"),
+    ({}, dict(segments=[(0, 64, 0), (100, 64, 1)]), sa.SA_E_VALUE, "multiple of kblock"),
+    ({}, dict(segments=[(0, 100, 0), (64, 64, 1)]), sa.SA_E_VALUE, "inside the previous segment"),
+    ({}, dict(segments=[(0, 64, 0), (192, 100, 1)]), sa.SA_E_VALUE, "rows 100 outside"),
+    ({}, dict(segments=[(0, 64, 0)], prefix_tokens=64), sa.SA_E_VALUE, "prefix_tokens must be 0"),
+    ({}, dict(segments=[(64 * x, 1, 0) for x in range(17)]), sa.SA_E_VALUE, "n_segments"),
 ])
 def test_route_validation(dims_kw, prm_kw, code, msg):
     assert _route(_dims(**dims_kw), _prm(**prm_kw)) == code

@@ -95,3 +95,14 @@ def test_full_sol_prefix_topk_2x32(sa, orc):
     wl = W.config(4)
     wl.rule, wl.sparsity = 1, 0.6
     _check_workload(orc, wl, sel=_sample(wl, 12, 7, frame_tokens=84 * 48, prefix=1024))
+
+
+def test_full_ref2va_segments(sa, orc):
+    """Reference-conditioned layout at full size (H=24, 17664 rows): text,
+    reference image and audio dense, reference and generated video routed."""
+    wl = W.ref2va_segments()
+    sel = _sample(wl, 12, 8)
+    seg_q = sorted({int(s[0]) // 128 for s in wl.segments})
+    nQB = wl.Lq // 128
+    sel = np.unique(np.concatenate([sel, np.array(seg_q, dtype=np.int64), (wl.H - 1) * nQB + np.array(seg_q)]))
+    _check_workload(orc, wl, sel=sel)

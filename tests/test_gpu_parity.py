@@ -266,3 +266,27 @@ def test_topk_prefix(sa, orc):
     wl = W.config(4, small=True)
     wl.rule, wl.sparsity = 1, 0.75
     _check_workload(orc, wl)
+
+
+def _segmented(**kw):
+    args = dict(H=2, text=77, ref_image=300, ref_audio=40, ref_video_frames=1, video_frames=2, frame_tokens=320)
+    args.update(kw)
+    return W.ref2va_segments(**args)
+
+
+@pytest.mark.parametrize("G,sparse_ref_video,kblock", [(1, True, 64), (2, False, 64), (1, True, 128)])
+def test_segmented_layout_threshold(sa, orc, G, sparse_ref_video, kblock):
+    """Dense text / image / audio segments, routed video segments, each padded
+    to a key-block boundary: several masked tiles per query block."""
+    wl = _segmented(centroids_per_block=G, sparse_reference_video=sparse_ref_video, kblock=kblock)
+    g, o = _check_workload(orc, wl)
+    first_routed = wl.segments[3][0] if sparse_ref_video else wl.segments[4][0]
+    assert (g["map"][..., :first_routed // kblock] != 2).all()
+
+
+@pytest.mark.parametrize("G", [1, 0])
+def test_segmented_layout_topk(sa, orc, G):
+    wl = _segmented(centroids_per_block=max(G, 1))
+    wl.centroids_per_block = G
+    wl.rule, wl.sparsity = 1, 0.75
+    _check_workload(orc, wl)
