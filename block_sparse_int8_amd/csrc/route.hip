@@ -587,8 +587,8 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_topk_kernel(RouteArg
 // Decisions with the proxies held in LDS.  When a query block has at most
 // kLdsCand candidates, one pass of matrix-core tiles writes s_ij for the 32
 // query blocks of a workgroup into a 32 x kLdsCand float64 array (128 KiB),
-// and every later pass reads it from there (slot j - jc0; NaN for blocks in
-// that range that are not candidates).  The rules and their arithmetic are
+// and every later pass reads it from there (slot j - jc0; NaN for slots that
+// hold no candidate).  The rules and their arithmetic are
 // those of the kernels above; only where s lives changes (and the summation
 // order of the mean and variance).  One workgroup per CU; kLdsWaves waves.
 // ---------------------------------------------------------------------------
@@ -598,33 +598,70 @@ constexpr int kLdsWaves = 8;
 template <int D, int NW>
 __device__ __forceinline__ void proxies_to_lds(const RouteArgs& a, const ProxyTiles<D>& pt, const CandRange& cr,
                                                int wave, double (*sv_s)[kLdsCand]) {
+  // at most kLdsCand / 32 + 1 column tiles, so at most MT per wave: all of a
+  // wave's key operands are loaded before the first product
+  constexpr int MT = (kLdsCand / 32 + 1 + NW - 1) / NW;
   const int t0 = cr.jc0 / 32, t1 = (cr.jc1 + 31) / 32;
-  typename ProxyTiles<D>::KOps kn;
-  if (t0 + wave < t1) pt.load_k(a, t0 + wave, kn);
-  for (int tt = t0 + wave; tt < t1; tt += NW) {
-    const typename ProxyTiles<D>::KOps kc = kn;
-    if (tt + NW < t1) pt.load_k(a, tt + NW, kn);
+  typename ProxyTiles<D>::KOps ko[MT];
+#pragma unroll
+  for (int u = 0; u < MT; ++u)
+    if (t0 + wave + u * NW < t1) pt.load_k(a, t0 + wave + u * NW, ko[u]);
+#pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int tt = t0 + wave + u * NW;
+    if (tt >= t1) break;
     double sv[16];
-    pt.tile(a, tt, kc, sv);
+    pt.tile(a, tt, ko[u], sv);
     const int j = tt * 32 + pt.n;
     if (j < cr.jc0 || j >= cr.jc1) continue;
     const bool cand = cr.has(j);
 #pragma unroll
     for (int e = 0; e < 16; ++e) sv_s[pt.row_of(e)][j - cr.jc0] = cand ? sv[e] : __builtin_nan("");
   }
+  // slots past the candidate range hold NaN too, so later passes read every slot
+  const int span = cr.jc1 - cr.jc0;
+  for (int x = threadIdx.x; x < 32 * kLdsCand; x += 64 * NW) {
+    const int r = x / kLdsCand, c = x % kLdsCand;
+    if (c >= span) sv_s[r][c] = __builtin_nan("");
+  }
+}
+
+// Classes of all key blocks (block_class) in LDS, filled once per workgroup.
+constexpr int kMaxRouteKB = 6144;   // key blocks per row accepted by the routing rules
+
+__device__ __forceinline__ void fill_classes(const RouteArgs& a, int nt, uint8_t* cls_s) {
+  for (int j = threadIdx.x; j < a.nKB; j += nt) cls_s[j] = (uint8_t)block_class(a.lay, j);
 }
 
 // Block states of the workgroup's query blocks: DROP for key blocks without
 // valid rows, EXACT for dense ones, cand_state(r, j - jc0) for candidates.  A
-// thread owns key blocks j, j + nt, ...; each store covers consecutive blocks
-// of one row.
+// thread owns groups of four consecutive key blocks of one row and writes the
+// four states with one store when the row allows it.
 template <typename F>
 __device__ __forceinline__ void write_map_rows(const RouteArgs& a, int64_t bh, int i0, const CandRange& cr, int nt,
-                                               F cand_state) {
-  for (int j = threadIdx.x; j < a.nKB; j += nt) {
-    const int cls = block_class(a.lay, j);
-    for (int r = 0; r < 32 && i0 + r < a.nQB; ++r)
-      a.map[(bh * a.nQB + i0 + r) * a.nKB + j] = cls < 2 ? (uint8_t)cls : cand_state(r, j - cr.jc0);
+                                               const uint8_t* cls_s, F cand_state) {
+  const int ng = (a.nKB + 3) / 4, rows = min(32, a.nQB - i0);
+  const bool wide = (a.nKB & 3) == 0 && (reinterpret_cast<uintptr_t>(a.map) & 3) == 0;   // 4-byte aligned rows
+  for (int x = threadIdx.x; x < ng * rows; x += nt) {
+    const int r = x / ng, j0 = (x % ng) * 4;
+    uint8_t* mrow = a.map + (bh * a.nQB + i0 + r) * a.nKB;
+    // four classes at once (cls_s has room past nKB; entries there are unused)
+    const uint32_t cl4 = *reinterpret_cast<const uint32_t*>(cls_s + j0);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t cls = (cl4 >> (8 * q)) & 255u;
+      const int c = min(max(j0 + q - cr.jc0, 0), kLdsCand - 1);   // any slot when not a candidate
+      const uint32_t cs = cand_state(r, c);
+      packed |= (cls < 2 ? cls : cs) << (8 * q);
+    }
+    if (wide) {
+      *reinterpret_cast<uint32_t*>(mrow + j0) = packed;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j0 + q < a.nKB) mrow[j0 + q] = (uint8_t)(packed >> (8 * q));
+    }
   }
 }
 
@@ -634,6 +671,7 @@ __global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
   __shared__ double sv_s[32][kLdsCand];
   __shared__ double thr_s[32];
   __shared__ int keep_s[32];
+  __shared__ __attribute__((aligned(4))) uint8_t cls_s[kMaxRouteKB + 4];
   const DecideItem wi(a);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t bh = (int64_t)wi.b * a.H + wi.h;
@@ -642,23 +680,37 @@ __global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
   const CandRange cr(a);
   const int N = cr.N;
   proxies_to_lds<D, NW>(a, pt, cr, wave, sv_s);
+  fill_classes(a, NT, cls_s);
   __syncthreads();
   // row r's mean and population variance: TPR adjacent lanes per row
-  const int r = t / TPR, part = t % TPR, span = cr.jc1 - cr.jc0;
-  double acc = 0.0;
-  for (int c = part; c < span; c += TPR) {
-    const double v = sv_s[r][c];
-    acc += __builtin_isnan(v) ? 0.0 : v;
-  }
+  const int r = t / TPR, part = t % TPR;
+  // kLdsCand / TPR slots per thread, read in batches of 8 into independent sums
+  constexpr int PER = kLdsCand / TPR;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-  for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  const double mu = N > 0 ? acc / N : __builtin_nan("");
-  double acc2 = 0.0;
-  for (int c = part; c < span; c += TPR) {
-    const double v = sv_s[r][c];
-    const double dl = v - mu;
-    acc2 += __builtin_isnan(v) ? 0.0 : dl * dl;
+  for (int c0 = 0; c0 < PER; c0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double v = sv_s[r][part + (c0 + u) * TPR];
+      acc[u] += __builtin_isnan(v) ? 0.0 : v;
+    }
   }
+  double sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  const double mu = N > 0 ? sum / N : __builtin_nan("");
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.0;
+#pragma unroll
+  for (int c0 = 0; c0 < PER; c0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double v = sv_s[r][part + (c0 + u) * TPR];
+      const double dl = v - mu;
+      acc[u] += __builtin_isnan(v) ? 0.0 : dl * dl;
+    }
+  }
+  double acc2 = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 #pragma unroll
   for (int o = TPR / 2; o >= 1; o >>= 1) acc2 += __shfl_xor(acc2, o, 64);
   if (part == 0) {
@@ -673,8 +725,8 @@ __global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  write_map_rows(a, bh, i0, cr, NT, [&](int rr, int c) -> uint8_t {
-    return (!keep_s[rr] && sv_s[rr][c] > thr_s[rr]) ? 2 : 1;
+  write_map_rows(a, bh, i0, cr, NT, cls_s, [&](int rr, int c) -> uint32_t {
+    return 1u + ((uint32_t)(keep_s[rr] == 0) & (uint32_t)(sv_s[rr][c] > thr_s[rr]));
   });
 }
 
@@ -694,6 +746,7 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
   __shared__ uint64_t phi_s[32];
   __shared__ uint32_t plo_s[32];
   __shared__ int nb_s[32];
+  __shared__ __attribute__((aligned(4))) uint8_t cls_s[kMaxRouteKB + 4];
   const DecideItem wi(a);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t bh = (int64_t)wi.b * a.H + wi.h;
@@ -707,6 +760,7 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
     a.stats[(bh * a.nQB + i0 + t) * 2] = __builtin_nan("");
     a.stats[(bh * a.nQB + i0 + t) * 2 + 1] = __builtin_nan("");
   }
+  fill_classes(a, NT, cls_s);
   if (select) {
     const ProxyTiles<D> pt(a, bh, i0, lane);
     proxies_to_lds<D, NW>(a, pt, cr, wave, sv_s);
@@ -767,19 +821,15 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
   }
   __syncthreads();
   // kept iff the key's first nb bits are >= the boundary prefix
-  write_map_rows(a, bh, i0, cr, NT, [&](int r, int c) -> uint8_t {
-    if (!select) return keep > 0 ? 1 : pruned;
+  write_map_rows(a, bh, i0, cr, NT, cls_s, [&](int r, int c) -> uint32_t {
+    if (!select) return keep > 0 ? 1u : (uint32_t)pruned;   // uniform
     const int nb = nb_s[r];
-    const uint64_t hi = order_key(sv_s[r][c]);
+    const uint64_t hi = order_key(sv_s[r][c]), ph = phi_s[r];
     const uint32_t lo = ~(uint32_t)(cr.jc0 + c);
-    bool ge;
-    if (nb <= 64) {
-      ge = nb == 0 || (hi >> (64 - nb)) >= phi_s[r];
-    } else {
-      const uint32_t lp = nb == 96 ? lo : lo >> (96 - nb);
-      ge = hi > phi_s[r] || (hi == phi_s[r] && lp >= plo_s[r]);
-    }
-    return ge ? 1 : pruned;
+    const uint64_t hp = nb == 0 ? 0ull : hi >> (64 - min(nb, 64));
+    const uint32_t lp = nb <= 64 ? 0u : (nb == 96 ? lo : lo >> (96 - nb));
+    const bool ge = nb <= 64 ? hp >= ph : ((hi > ph) | ((hi == ph) & (lp >= plo_s[r])));
+    return ge ? 1u : (uint32_t)pruned;
   });
 }
 
