@@ -111,7 +111,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-stride", type=int, default=80)
+    ap.add_argument("--cpu-sample-stride", type=int, default=40)
     ap.add_argument("--heads", type=int, default=40, help="heads (40 for the measured workload)")
     ap.add_argument("--rule", choices=["threshold", "topk"], default="threshold",
                     help="routing rule: Sol threshold 1.0 (the measured workload) or fixed sparsity")
