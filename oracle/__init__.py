@@ -35,6 +35,7 @@ def _lib():
         _LIB = ctypes.CDLL(path)
         _LIB.orc_num_threads.restype = ctypes.c_int
         _LIB.orc_route.restype = ctypes.c_int
+        _LIB.orc_cache_append.restype = ctypes.c_int
     return _LIB
 
 
@@ -58,6 +59,25 @@ def quantize(x_bits: np.ndarray, valid_len: Optional[int] = None, rows_per_block
     _lib().orc_quantize(_p(x), ctypes.c_int64(H * L * d), ctypes.c_int64(L * d), ctypes.c_int64(d),
                         B, H, L, d, valid_len, rows_per_block, _p(q), _p(s))
     return q, s
+
+
+def cache_append(cache_q: np.ndarray, cache_scale: np.ndarray, x_bits: np.ndarray, first_slot: int,
+                 valid_len: Optional[int] = None, rows_per_slab: int = 128):
+    """Streaming INT8 cache: quantize the bf16 chunk [B,H,rows,d] per slab and
+    write slab s into ring slot (first_slot + s) % slots of ``cache_q``
+    [B,H,slots*R,d] / ``cache_scale`` [B,H,slots] (updated in place)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    B, H, rows, d = x.shape
+    slots = cache_scale.shape[2]
+    assert cache_q.flags.c_contiguous and cache_scale.flags.c_contiguous
+    assert cache_q.dtype == np.int8 and cache_scale.dtype == np.float32
+    valid_len = rows if valid_len is None else valid_len
+    rc = _lib().orc_cache_append(_p(x), ctypes.c_int64(H * rows * d), ctypes.c_int64(rows * d), ctypes.c_int64(d),
+                                 B, H, rows, d, valid_len, rows_per_slab, _p(cache_q), _p(cache_scale), slots,
+                                 first_slot)
+    if rc != 0:
+        raise ValueError("oracle cache_append rejected its arguments")
+    return cache_q, cache_scale
 
 
 def _segments(segments):

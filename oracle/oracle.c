@@ -129,6 +129,42 @@ static double v_at(const orc_vsrc* s, int b, int h, int r, int c) {
 }
 
 /* ------------------------------------------------------------------------- */
+/* Streaming INT8 K/V cache (FlashVSR Kitchen Sparse Attention, opening      */
+/* section: the streaming modes keep a sliding cache of past K/V in every   */
+/* block, stored as INT8 in bounded 128-row slabs).  The cache is a ring of  */
+/* `slots` slabs of R rows per (b, h).  A chunk of `rows` new rows is        */
+/* quantized per slab of R rows exactly as orc_quantize does (rows at or     */
+/* past valid_len are padding), and slab s of the chunk replaces ring slot   */
+/* (first_slot + s) mod slots, evicting what that slot held; other slots are */
+/* left as they are.                                                          */
+/* Pinned by: a stream appended in several chunks leaves the ring equal to   */
+/* one quantization of the whole stream, slab g in slot g mod slots, for the */
+/* last `slots` slabs; untouched slots keep their contents.                  */
+/* Returns 0, or -1 on bad arguments.                                         */
+/* ------------------------------------------------------------------------- */
+int orc_cache_append(const uint16_t* x, int64_t sB, int64_t sH, int64_t sL, int B, int H, int rows, int d,
+                     int valid_len, int R, int8_t* cache_q, float* cache_scale, int slots, int first_slot) {
+  if (rows % R || rows / R > slots || first_slot < 0 || first_slot >= slots) return -1;
+  int nblk = rows / R;
+  int8_t* q = (int8_t*)malloc((size_t)B * H * (rows > 0 ? rows : 1) * d);
+  float* sc = (float*)malloc(sizeof(float) * (size_t)B * H * (nblk > 0 ? nblk : 1));
+  orc_quantize(x, sB, sH, sL, B, H, rows, d, valid_len, R, q, sc);
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      int64_t bh = (int64_t)b * H + h;
+      for (int s = 0; s < nblk; ++s) {
+        int slot = (first_slot + s) % slots;
+        memcpy(cache_q + (bh * slots + slot) * (int64_t)R * d, q + (bh * rows + (int64_t)s * R) * d,
+               (size_t)R * d);
+        cache_scale[bh * slots + slot] = sc[bh * nblk + s];
+      }
+    }
+  free(q);
+  free(sc);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Key layout.  Ref2VA VSA, two-stage attention patch: the geometry mapper    */
 /* gives the text, reference-image and reference-audio tokens tiles of their */
 /* own, which stay dense, and only the generated-video key tiles are pruned; */
