@@ -4,7 +4,8 @@ Argument marshalling only: every step of the computation runs in the library's
 gfx950 HIP kernels.  PyTorch supplies device memory and the current HIP stream.
 The entry points keep the C names:
 
-    quantize_qk_int8, sparse_attn_route, sparse_attn_fwd, gather_virtual_kv
+    quantize_qk_int8, sparse_attn_route, sparse_attn_fwd, gather_virtual_kv,
+    kv_cache_append_int8
 
 plus ``sparse_attention`` which chains quantize -> route -> fwd.
 
@@ -22,7 +23,7 @@ from typing import Optional, Sequence
 
 import torch
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 SA_OK, SA_E_NULL, SA_E_SHAPE, SA_E_ALIGN, SA_E_VALUE, SA_E_UNSUPPORTED, SA_E_DEVICE, SA_E_LAUNCH, SA_E_WORKSPACE = range(9)
 SA_DROP, SA_EXACT, SA_CENTROID = 0, 1, 2
 SA_BF16, SA_INT8, SA_F32 = 0, 1, 2
@@ -97,6 +98,8 @@ def load(path: Optional[str] = None):
     lib.sparse_attn_fwd.restype = i32
     lib.gather_virtual_kv.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     lib.gather_virtual_kv.restype = i32
+    lib.kv_cache_append_int8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, i32, i32, vp]
+    lib.kv_cache_append_int8.restype = i32
     if path is None:
         _LIB = lib
     return lib
@@ -157,6 +160,27 @@ def quantize_qk_int8(x: torch.Tensor, valid_len: Optional[int] = None, rows_per_
     _check(load().quantize_qk_int8(_ptr(x), x.stride(0), x.stride(1), x.stride(2), B, H, L, d, valid_len,
                                    rows_per_block, _ptr(out), _ptr(scale), _stream(stream)))
     return out, scale
+
+
+def kv_cache_append_int8(x: torch.Tensor, cache_q: torch.Tensor, cache_scale: torch.Tensor, first_slot: int,
+                         valid_len: Optional[int] = None, rows_per_slab: int = 128, stream=None):
+    """Quantize the bf16 chunk x [B,H,rows,d] per slab into ring slots
+    (first_slot + s) % slots of cache_q int8 [B,H,slots*R,d] and cache_scale
+    fp32 [B,H,slots], in place.  Returns the next free slot."""
+    if x.dim() != 4:
+        raise ValueError("x must be [B,H,rows,d]")
+    _need(x, "x", torch.bfloat16, contiguous=False)
+    B, H, rows, d = x.shape
+    if x.stride(3) != 1:
+        raise ValueError("x must have a contiguous channel dimension")
+    slots = cache_scale.shape[2]
+    _need(cache_q, "cache_q", torch.int8, (B, H, slots * rows_per_slab, d))
+    _need(cache_scale, "cache_scale", torch.float32, (B, H, slots))
+    valid_len = rows if valid_len is None else valid_len
+    _check(load().kv_cache_append_int8(_ptr(x), x.stride(0), x.stride(1), x.stride(2), B, H, rows, d, valid_len,
+                                       rows_per_slab, _ptr(cache_q), _ptr(cache_scale), slots, first_slot,
+                                       _stream(stream)))
+    return (first_slot + rows // rows_per_slab) % slots
 
 
 def _dims(B, H, Lq, Lkv, d, lq_valid, lkv_valid, Lv):

@@ -179,8 +179,34 @@ int32_t quantize_qk_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL,
     return fail(SA_E_ALIGN, "quantize_qk_int8: strides must be multiples of 8 elements and sL >= d");
   if (const int32_t rc = check_current_device()) return rc;
   if (L == 0) return ok();
-  sa::QuantizeArgs a{static_cast<const uint16_t*>(x_bf16), sB, sH, sL, B, H, L, d, valid_len, rows_per_block, x_q, scale};
+  sa::QuantizeArgs a{static_cast<const uint16_t*>(x_bf16), sB, sH, sL, B, H, L, d, valid_len, rows_per_block, x_q, scale,
+                     L / rows_per_block, 0};
   return launched(sa::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize");
+}
+
+int32_t kv_cache_append_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL, int32_t B, int32_t H,
+                             int32_t rows, int32_t d, int32_t valid_len, int32_t rows_per_slab, int8_t* cache_q,
+                             float* cache_scale, int32_t slots, int32_t first_slot, void* stream) {
+  if (!x_bf16 || !cache_q || !cache_scale)
+    return fail(SA_E_NULL, "kv_cache_append_int8: x, cache_q and cache_scale must not be NULL");
+  if (B < 1 || H < 1 || rows < 0) return fail(SA_E_SHAPE, "kv_cache_append_int8: bad B/H/rows (%d, %d, %d)", B, H, rows);
+  if (d != 64 && d != 128) return fail(SA_E_SHAPE, "kv_cache_append_int8: d must be 64 or 128 (got %d)", d);
+  if (rows_per_slab != 64 && rows_per_slab != 128)
+    return fail(SA_E_VALUE, "kv_cache_append_int8: rows_per_slab must be 64 or 128 (got %d)", rows_per_slab);
+  if (rows % rows_per_slab) return fail(SA_E_SHAPE, "kv_cache_append_int8: rows (%d) must be a multiple of rows_per_slab", rows);
+  if (slots < 1 || rows / rows_per_slab > slots)
+    return fail(SA_E_SHAPE, "kv_cache_append_int8: %d slabs do not fit a ring of %d slots", rows / rows_per_slab, slots);
+  if (first_slot < 0 || first_slot >= slots)
+    return fail(SA_E_VALUE, "kv_cache_append_int8: first_slot %d outside [0, %d)", first_slot, slots);
+  if (valid_len < 0 || valid_len > rows) return fail(SA_E_SHAPE, "kv_cache_append_int8: valid_len %d outside [0, %d]", valid_len, rows);
+  if (!aligned16(x_bf16) || !aligned16(cache_q)) return fail(SA_E_ALIGN, "kv_cache_append_int8: x and cache_q must be 16-byte aligned");
+  if (sB % 8 || sH % 8 || sL % 8 || sL < d)
+    return fail(SA_E_ALIGN, "kv_cache_append_int8: strides must be multiples of 8 elements and sL >= d");
+  if (const int32_t rc = check_current_device()) return rc;
+  if (rows == 0) return ok();
+  sa::QuantizeArgs a{static_cast<const uint16_t*>(x_bf16), sB, sH, sL, B, H, rows, d, valid_len, rows_per_slab, cache_q,
+                     cache_scale, slots, first_slot};
+  return launched(sa::launch_quantize(a, static_cast<hipStream_t>(stream)), "kv_cache_append_int8");
 }
 
 size_t sparse_attn_route_workspace_size(const sa_dims* dims, const sa_route_params* p, int32_t has_explicit_map) {

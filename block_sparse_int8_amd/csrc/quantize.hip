@@ -11,15 +11,20 @@
 // slabs): scale = amax/127; code = clamp(rint(x * (127/amax)), -127, 127) with
 // IEEE float32 division, one multiply and round-half-even; an all-zero block has
 // scale 0; rows at or past the valid length get code 0 and are left out of amax.
+// The streaming cache (same opening section: a sliding INT8 cache of past K/V
+// per block) writes each block into a ring slot of a slab tensor instead.
 #include "sa_device.h"
 #include "sa_launch.h"
 
 namespace sa {
 
+// Source block blk is written to destination block (first + blk) mod nslots of
+// a tensor of nslots blocks: the identity for a plain quantization (first = 0,
+// nslots = L / R), a ring position for the streaming cache.
 template <int D, int R>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t sB,
-                                                       int64_t sH, int64_t sL, int H, int L,
-                                                       int valid_len, int8_t* __restrict__ q,
+                                                       int64_t sH, int64_t sL, int H, int valid_len,
+                                                       int nslots, int first, int8_t* __restrict__ q,
                                                        float* __restrict__ scale) {
   constexpr int VPR = D / 8;            // 16-byte vectors per row
   constexpr int NV = R * VPR / 256;     // vectors per thread
@@ -50,13 +55,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-  const int nblk = L / R;
-  if (t == 0) scale[((int64_t)b * H + h) * nblk + blk] = amax / 127.0f;
-  int8_t* qb = q + ((int64_t)b * H + h) * L * D;
+  const int slot = (first + blk) % nslots;
+  if (t == 0) scale[((int64_t)b * H + h) * nslots + slot] = amax / 127.0f;
+  int8_t* qb = q + (((int64_t)b * H + h) * nslots + slot) * R * D;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int v = t + 256 * i, row = blk * R + v / VPR, cc = v % VPR;
-    *reinterpret_cast<uint64_t*>(qb + (int64_t)row * D + cc * 8) = quant8(vals[i], inv, valid[i]);
+    const int v = t + 256 * i, r = v / VPR, cc = v % VPR;
+    *reinterpret_cast<uint64_t*>(qb + (int64_t)r * D + cc * 8) = quant8(vals[i], inv, valid[i]);
   }
 }
 
@@ -126,9 +131,11 @@ template <int D>
 static hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t st) {
   dim3 grid(a.L / a.R, a.H, a.B);
   if (a.R == 64)
-    quantize_kernel<D, 64><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.L, a.valid_len, a.q, a.scale);
+    quantize_kernel<D, 64><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.valid_len, a.nslots, a.first, a.q,
+                                                 a.scale);
   else
-    quantize_kernel<D, 128><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.L, a.valid_len, a.q, a.scale);
+    quantize_kernel<D, 128><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.valid_len, a.nslots, a.first, a.q,
+                                                  a.scale);
   return hipGetLastError();
 }
 

@@ -55,6 +55,7 @@ struct QuantizeArgs {
   int B, H, L, d, valid_len, R;
   int8_t* q;
   float* scale;
+  int nslots, first;   // destination: block b goes to slot (first + b) % nslots of q / scale
 };
 
 struct GatherArgs {

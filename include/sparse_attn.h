@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 3
+#define SA_ABI_VERSION 4
 
 enum sa_status {
   SA_OK = 0,
@@ -156,6 +156,27 @@ int32_t sa_device_check(int32_t device);
 int32_t quantize_qk_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL, int32_t B,
                          int32_t H, int32_t L, int32_t d, int32_t valid_len,
                          int32_t rows_per_block, int8_t* x_q, float* scale, void* stream);
+
+/* Streaming INT8 K/V cache append (FlashVSR Kitchen Sparse Attention, opening
+ * section: the streaming modes keep a sliding cache of past K/V in every
+ * block, stored as INT8 in bounded 128-row slabs).  The cache of one tensor (K
+ * or V) is a ring of `slots` slabs of rows_per_slab rows per (b, h).  The new
+ * chunk is quantized per slab exactly as quantize_qk_int8 quantizes blocks, and
+ * slab s of it replaces ring slot (first_slot + s) mod slots, evicting the slab
+ * there; other slots are not touched.  The caller tracks which slot holds which
+ * slab: route and forward see the ring in slot order, so maps and segments
+ * passed with it refer to slot order (attention is order-free over keys).
+ *   x_bf16       bf16 chunk, element (b,h,l,c) at x_bf16 + b*sB + h*sH + l*sL + c
+ *                (strides in elements, multiples of 8; channel stride 1)
+ *   rows         chunk rows, a multiple of rows_per_slab, rows/rows_per_slab <= slots
+ *   valid_len    rows at or past it are padding (code 0, not in amax)
+ *   rows_per_slab 64 or 128
+ *   cache_q      int8 [B,H,slots*rows_per_slab,d]; cache_scale fp32 [B,H,slots]
+ *   first_slot   in [0, slots)
+ * Bit-exact with quantizing the chunk and copying its slabs into the ring. */
+int32_t kv_cache_append_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL, int32_t B, int32_t H,
+                             int32_t rows, int32_t d, int32_t valid_len, int32_t rows_per_slab, int8_t* cache_q,
+                             float* cache_scale, int32_t slots, int32_t first_slot, void* stream);
 
 /* Bytes of device workspace sparse_attn_route needs for these arguments (0 when
  * an explicit map is given).  Returns 0 and sets the error text on bad input. */

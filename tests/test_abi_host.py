@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_header_declares_the_four_calls():
     names = _declared_functions()
-    for n in ("quantize_qk_int8", "sparse_attn_route", "sparse_attn_fwd", "gather_virtual_kv",
+    for n in ("quantize_qk_int8", "sparse_attn_route", "sparse_attn_fwd", "gather_virtual_kv", "kv_cache_append_int8",
               "sa_abi_version", "sa_last_error", "sa_device_check", "sparse_attn_route_workspace_size"):
         assert n in names, n
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 3
+    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 4
 
 
 def test_missing_library_lists_search_paths(monkeypatch, tmp_path):
@@ -202,3 +202,21 @@ def test_topk_rule_without_centroids_passes_validation():
     need = _lib().sparse_attn_route_workspace_size(ctypes.byref(dims), ctypes.byref(prm), 0)
     assert need > 0
     assert _route(dims, prm, ws=ctypes.c_void_p(256), wsb=need, G_out=False) == sa.SA_E_DEVICE
+
+
+def test_cache_append_validation():
+    lib = _lib()
+    p = ctypes.c_void_p(256)
+    ok = dict(rows=256, d=128, valid=256, R=128, slots=4, first=0)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.kv_cache_append_int8(p, 0, 0, 128, 1, 1, a["rows"], a["d"], a["valid"], a["R"], p, p, a["slots"],
+                                         a["first"], None)
+    assert call(rows=200, valid=200) == sa.SA_E_SHAPE          # not whole slabs
+    assert call(slots=1) == sa.SA_E_SHAPE                      # 2 slabs into a ring of 1
+    assert call(first=4) == sa.SA_E_VALUE
+    assert call(first=-1) == sa.SA_E_VALUE
+    assert call(R=32) == sa.SA_E_VALUE
+    assert call(valid=300) == sa.SA_E_SHAPE
+    assert call(d=96) == sa.SA_E_SHAPE
+    assert lib.kv_cache_append_int8(None, 0, 0, 128, 1, 1, 256, 128, 256, 128, p, p, 4, 0, None) == sa.SA_E_NULL

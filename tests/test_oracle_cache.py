@@ -58,3 +58,37 @@ def test_rejects_overfull_chunk(orc):
     cs = np.zeros((1, 1, 4), np.float32)
     with pytest.raises(ValueError):
         orc.cache_append(cq, cs, x, first_slot=0)
+
+
+def test_attention_over_ring_in_slot_order_equals_time_order(orc):
+    """Keys in ring (slot) order with the map permuted the same way give the
+    attention of the time-ordered keys: the softmax is order-free over keys."""
+    from workloads import EXACT
+    H, d, R, F, T = 1, 64, 128, 256, 4
+    slots, bpf = 2 * F // R, F // R
+    rng = np.random.default_rng(44)
+    q_all, k_all, v_all = (bf16_bits(rng.standard_normal((1, H, T * F, d)).astype(np.float32)) for _ in range(3))
+    kq = np.zeros((1, H, slots * R, d), np.int8)
+    ks = np.zeros((1, H, slots), np.float32)
+    vq, vs = kq.copy(), ks.copy()
+    slot = 0
+    for t in range(T):
+        fr = slice(t * F, (t + 1) * F)
+        orc.cache_append(kq, ks, k_all[:, :, fr], slot)
+        orc.cache_append(vq, vs, v_all[:, :, fr], slot)
+        slot = (slot + bpf) % slots
+    order = np.array([((T - 2) * bpf + j) % slots for j in range(slots)])   # slot of each time-ordered slab
+    lmap = np.full((1, H, bpf, slots), EXACT, np.uint8)
+    lmap[..., 0] = 0
+    smap = np.zeros_like(lmap)
+    smap[..., order] = lmap
+    o8, osc = orc.quantize(q_all[:, :, (T - 1) * F:], rows_per_block=128)
+    idx = np.concatenate([np.arange(s * R, (s + 1) * R) for s in order])
+    a = orc.forward(o8, osc, kq[:, :, idx], ks[:, :, order], 128, F, slots * R, lmap, v8=vq[:, :, idx],
+                    v_scale=vs[:, :, order], v_scale_rows=128, kblock=128, G=0)[0]
+    b = orc.forward(o8, osc, kq, ks, 128, F, slots * R, smap, v8=vq, v_scale=vs, v_scale_rows=128, kblock=128,
+                    G=0)[0]
+    assert np.abs(a - b).max() < 1e-12
+    # and the ring holds the last two frames, quantized per slab
+    kq_ref, _ = orc.quantize(k_all[:, :, (T - 2) * F:], rows_per_block=R)
+    assert np.array_equal(kq[:, :, idx], kq_ref)
