@@ -105,6 +105,64 @@ def cpu_baseline(wl, sample_stride: int):
                 threads=oracle.num_threads(), sel=sel, out=out, map=r["map"], tie=r["tie"])
 
 
+def bench_cache_append(args, sa, W):
+    """Streaming INT8 cache: append the newest frame's K and V (12 heads x 2048
+    rows x 128) into rings of 64 slabs (four frames), and a whole four-frame
+    chunk.  One JSON line; value = HBM bytes the appends must move / time."""
+    import torch
+    H, d, F, slots = 12, 128, 2048, 64
+    rng = np.random.default_rng(2)
+    frames = torch.from_numpy(W.bf16_bits(rng.standard_normal((1, H, 4 * F, d), dtype=np.float32)).view(np.int16))
+    k = frames.view(torch.bfloat16).cuda()
+    v = k.flip(2).contiguous()
+    kq = torch.zeros((1, H, slots * 128, d), dtype=torch.int8, device="cuda")
+    ks = torch.zeros((1, H, slots), dtype=torch.float32, device="cuda")
+    vq, vs = torch.zeros_like(kq), torch.zeros_like(ks)
+    stream = torch.cuda.current_stream()
+
+    def run(rows, reps):
+        """us per append (one tensor), timed over replays of a captured HIP graph
+        of `reps` K and V appends so host launch overhead is not in the time."""
+        slot = 0
+        for _ in range(args.warmup):
+            sa.kv_cache_append_int8(k[:, :, :rows], kq, ks, slot)
+            slot = sa.kv_cache_append_int8(v[:, :, :rows], vq, vs, slot)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                s_ = slot
+                for _ in range(reps):
+                    sa.kv_cache_append_int8(k[:, :, :rows], kq, ks, s_, stream=side)
+                    s_ = sa.kv_cache_append_int8(v[:, :, :rows], vq, vs, s_, stream=side)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (2 * reps)
+
+    reps = max(args.steps, 1) * 20
+    t1, t4 = run(F, reps), run(4 * F, reps)
+    per = lambda rows: H * rows * d * 3 + H * (rows // 128) * 4
+    res = {"metric": "streaming INT8 K/V cache append GB/s (FlashVSR-like: H=12, d=128, 2048-row frames)",
+           "value": round(per(4 * F) / (t4 * 1e-6) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 in, int8 + fp32 scale out", "data": "synthetic (seeded N(0,1) bf16)",
+           "config": {"workload": "kv_cache_append_int8 of K and V into rings of 64 slabs of 128 rows",
+                      "H": H, "d": d, "frame_rows": F, "slots": slots},
+           "us_per_append": {"one_frame": round(t1, 2), "four_frames": round(t4, 2)},
+           "GB/s": {"one_frame": round(per(F) / (t1 * 1e-6) / 1e9, 1),
+                    "four_frames": round(per(4 * F) / (t4 * 1e-6) / 1e9, 1)},
+           "frac_of_8TB/s": round(per(4 * F) / (t4 * 1e-6) / 1e9 / PEAK_HBM, 4)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +174,9 @@ def main():
     ap.add_argument("--rule", choices=["threshold", "topk"], default="threshold",
                     help="routing rule: Sol threshold 1.0 (the measured workload) or fixed sparsity")
     ap.add_argument("--sparsity", type=float, default=0.75, help="pruned fraction for --rule topk")
+    ap.add_argument("--cache-append", action="store_true",
+                    help="measure the streaming INT8 K/V cache append instead (FlashVSR-like: H=12, frames of "
+                         "2048 rows, a ring of four frames)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scales HBM counters under rocprofv3)")
     args = ap.parse_args()
@@ -129,6 +190,9 @@ def main():
     import workloads as W
 
     sa.device_check(0)
+    if args.cache_append:
+        bench_cache_append(args, sa, W)
+        return
     t = time.perf_counter()
     wl = W.wan_like(H=args.heads)
     topk = args.rule == "topk"
