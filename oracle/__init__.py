@@ -142,8 +142,10 @@ def route(q8, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, *, v_bits=None, v8
 def forward(q8, q_scale, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, block_map, *, kbar=None,
             vbar=None, count=None, v_bits=None, v8=None, v_scale=None, v_scale_rows=128,
             v_block_src=None, kblock=64, G=1, sm_scale=None, sel: Optional[Sequence[int]] = None,
-            segments=None):
+            segments=None, q_bits=None, k_bits=None):
     """Attention output for the selected query blocks (all when ``sel`` is None).
+    With ``q_bits``/``k_bits`` (bf16 [B,H,L,d]) the exact logits and the
+    centroid logits use the bf16 Q/K (the floating QK path).
     ``sel`` entries are (b*H + h)*nQB + i.  Returns (out float64 [nsel,128,d],
     lse float64 [nsel,128], sel)."""
     q8 = np.ascontiguousarray(q8, dtype=np.int8)
@@ -177,7 +179,9 @@ def forward(q8, q_scale, k8, k_scale, k_scale_rows, lq_valid, lkv_valid, block_m
                        _p(np.ascontiguousarray(kbar, dtype=np.float64)),
                        _p(np.ascontiguousarray(vbar, dtype=np.float64)),
                        _p(np.ascontiguousarray(count, dtype=np.float64)), ctypes.c_double(sm),
-                       _p(sel), len(sel), _p(out), _p(lse))
+                       _p(sel), len(sel), _p(out), _p(lse),
+                       _p(None if q_bits is None else np.ascontiguousarray(q_bits, dtype=np.uint16)),
+                       _p(None if k_bits is None else np.ascontiguousarray(k_bits, dtype=np.uint16)))
     return out, lse, sel
 
 
@@ -220,6 +224,8 @@ def run(wl, sel=None, tau=None):
     (k_scale_rows blocks, or the virtual-KV gather), quantize V when it is an
     INT8 cache, route, then the forward pass over ``sel``."""
     tau = wl.threshold if tau is None else tau
+    if wl.qk_float and (wl.virtual or wl.v_int8):
+        raise ValueError("the floating QK path takes bf16 Q, K and V")
     q8, qs = quantize(wl.q, wl.lq_valid, 128)
     vbs = None
     if wl.virtual:
@@ -240,6 +246,7 @@ def run(wl, sel=None, tau=None):
     out, lse, sel = forward(q8, qs, k8, ks, wl.k_scale_rows, wl.lq_valid, wl.lkv_valid, r["map"],
                             kbar=r["kbar"], vbar=r["vbar"], count=r["count"], v_block_src=vbs,
                             kblock=wl.kblock, G=wl.centroids_per_block, sm_scale=wl.sm_scale, sel=sel,
-                            segments=wl.segments, **vkw)
+                            segments=wl.segments, q_bits=wl.q if wl.qk_float else None,
+                            k_bits=wl.k if wl.qk_float else None, **vkw)
     return dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, v_block_src=vbs, out=out, lse=lse, sel=sel, **r,
                 **{k: v for k, v in vkw.items() if k != "v_bits"})

@@ -435,9 +435,16 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
 /* Rows with nothing to attend, and rows past lq_valid, give 0 and -inf.     */
 /* sel lists query blocks as (b*H + h)*nQB + i; out is [nsel][128][d],       */
 /* lse [nsel][128].                                                           */
+/* Floating QK path (q_bf16, k_bf16 given; Configure Sol Sparse Attention,  */
+/* "How it works": with a floating dense backend the exact blocks run in    */
+/* floating point instead of W8A8): x_tu = sm * (q_t . k_u) and              */
+/* c_tg = sm * (q_t . kbar_g) on the bf16 values; the block map and the     */
+/* centroids are the same (routed on the INT8 codes).                        */
 /* Pinned by: all-exact map == textbook softmax attention (library SDPA in   */
 /* float64), LCSA map == masked dense attention, single-block centroid       */
-/* closed forms, identical-key blocks (centroid == exact, count weighting).  */
+/* closed forms, identical-key blocks (centroid == exact, count weighting);  */
+/* the floating path: all-exact == SDPA on the bf16 inputs, a single        */
+/* centroid block gives vbar.                                                 */
 /* ------------------------------------------------------------------------- */
 void orc_forward(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                  int k_scale_rows, const uint16_t* v_bf16, const int8_t* v_i8, const float* v_scale,
@@ -445,7 +452,8 @@ void orc_forward(const int8_t* q, const float* q_scale, const int8_t* k, const f
                  int d, int lq_valid, int lkv_valid, int kblock, const int32_t* seg, int nseg, int G,
                  const uint8_t* map,
                  const double* kbar, const double* vbar, const double* count, double sm_scale,
-                 const int64_t* sel, int nsel, double* out, double* lse) {
+                 const int64_t* sel, int nsel, double* out, double* lse, const uint16_t* q_bf16,
+                 const uint16_t* k_bf16) {
   int nQB = (Lq + QBLOCK - 1) / QBLOCK;
   int nKB = (Lkv + kblock - 1) / kblock;
   int nKS = (Lkv + k_scale_rows - 1) / k_scale_rows;
@@ -475,11 +483,22 @@ void orc_forward(const int8_t* q, const float* q_scale, const int8_t* k, const f
         lse[(int64_t)e * QBLOCK + r] = -INFINITY;
         if (t >= Lq || t >= lq_valid) continue;
         const int8_t* qt = q + (bh * Lq + t) * d;
+        const uint16_t* qf = q_bf16 ? q_bf16 + (bh * Lq + t) * d : NULL;
         int n = 0;
         for (int j = 0; j < nKB; ++j) {
           if (mrow[j] == ORC_EXACT) {
             for (int u = j * kblock; u < (j + 1) * kblock && u < Lkv; ++u) {
               if (!orc_key_valid(&lay, u)) continue;
+              if (qf) {
+                const uint16_t* kf = k_bf16 + (bh * Lkv + u) * d;
+                double dotf = 0.0;
+                for (int c = 0; c < d; ++c) dotf += (double)bf16_to_f32(qf[c]) * (double)bf16_to_f32(kf[c]);
+                x[n] = sm_scale * dotf;
+                w[n] = 1.0;
+                col[n] = u;
+                ++n;
+                continue;
+              }
               const int8_t* ku = k + (bh * Lkv + u) * d;
               int64_t dot = 0;
               for (int c = 0; c < d; ++c) dot += (int64_t)qt[c] * ku[c];
@@ -493,7 +512,11 @@ void orc_forward(const int8_t* q, const float* q_scale, const int8_t* k, const f
               int64_t ci = (bh * nKB + j) * G + g;
               if (count[ci] <= 0.0) continue;
               double dot = 0.0;
-              for (int c = 0; c < d; ++c) dot += a * (double)qt[c] * kbar[ci * d + c];
+              if (qf) {
+                for (int c = 0; c < d; ++c) dot += (double)bf16_to_f32(qf[c]) * kbar[ci * d + c];
+              } else {
+                for (int c = 0; c < d; ++c) dot += a * (double)qt[c] * kbar[ci * d + c];
+              }
               x[n] = sm_scale * dot;
               w[n] = count[ci];
               col[n] = (int)(-1 - ci);

@@ -191,3 +191,44 @@ def test_centroid_mix_matches_explicit_logit_softmax(orc):
         p = torch.softmax(torch.from_numpy(logit), dim=-1).numpy()
         ref = p @ np.array(cols_v)
         assert np.abs(out[i] - ref).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Floating QK path (Configure Sol Sparse Attention, "How it works": with a
+# floating dense backend the exact blocks run in floating point, not W8A8).
+# ---------------------------------------------------------------------------
+
+def test_float_path_all_exact_is_softmax_attention_on_bf16(orc):
+    wl = W.tiny_sol(seed=23, H=2, L=512, d=64, valid=450)
+    q8, qs = orc.quantize(wl.q, wl.lq_valid, 128)
+    k8, ks = orc.quantize(wl.k, wl.lkv_valid, 64)
+    r = orc.route(q8, k8, ks, 64, wl.lq_valid, wl.lkv_valid, v_bits=wl.v, tau=float("inf"), G=1)
+    out, lse, _ = orc.forward(q8, qs, k8, ks, 64, wl.lq_valid, wl.lkv_valid, r["map"], kbar=r["kbar"],
+                              vbar=r["vbar"], count=r["count"], v_bits=wl.v, q_bits=wl.q, k_bits=wl.k)
+    qf, kf, vf = (bf16_to_f32(t)[0].astype(np.float64) for t in (wl.q, wl.k, wl.v))
+    mask = np.zeros((512, 512), bool)
+    mask[:, :wl.lkv_valid] = True
+    ref = _sdpa(qf, kf, vf, mask)
+    got = _blocks_to_rows(out, 4)
+    assert np.abs(got[:, :wl.lq_valid] - ref[:, :wl.lq_valid]).max() < 1e-12
+    logits = np.einsum("hqd,hkd->hqk", qf, kf) / math.sqrt(64)
+    ref_lse = torch.logsumexp(torch.from_numpy(logits[:, :, :wl.lkv_valid]), dim=-1).numpy()
+    assert np.abs(lse.reshape(2, 512)[:, :wl.lq_valid] - ref_lse[:, :wl.lq_valid]).max() < 1e-10
+    # the INT8 path differs from it by the quantization error only
+    o8, _, _ = orc.forward(q8, qs, k8, ks, 64, wl.lq_valid, wl.lkv_valid, r["map"], kbar=r["kbar"],
+                           vbar=r["vbar"], count=r["count"], v_bits=wl.v)
+    diff = np.abs(_blocks_to_rows(o8, 4) - got)[:, :wl.lq_valid]
+    assert 0 < diff.max() < 0.1
+
+
+def test_float_path_single_centroid_block_outputs_vbar(orc):
+    q, k, v, n = _one_block_case()
+    Lq = q.shape[2]
+    q8, qs = orc.quantize(q, Lq, 128)
+    k8, ks = orc.quantize(k, n, 64)
+    em = np.full((1, 1, Lq // 128, 1), CENTROID, np.uint8)
+    r = orc.route(q8, k8, ks, 64, Lq, n, v_bits=v, G=1, kblock=64, explicit_map=em, map_kblock=64)
+    out, _, _ = orc.forward(q8, qs, k8, ks, 64, Lq, n, r["map"], kbar=r["kbar"], vbar=r["vbar"],
+                            count=r["count"], v_bits=v, G=1, q_bits=q, k_bits=k)
+    vbar = bf16_to_f32(v)[0, 0, :n].astype(np.float64).mean(0)
+    assert np.abs(out.reshape(Lq, -1) - vbar[None]).max() < 1e-14

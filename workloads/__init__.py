@@ -67,6 +67,7 @@ class Workload:
     centroids_per_block: int = 1
     prefix_tokens: int = 0
     segments: Optional[np.ndarray] = None      # int32 [n, 3] key layout: start, rows, routed (replaces the prefix)
+    qk_float: bool = False             # exact tiles on the bf16 Q/K (floating QK path) instead of INT8
     kblock: int = 64
     k_scale_rows: int = 64
     v_int8: bool = False               # V handed over as an INT8 cache (quantized per v_scale_rows)
