@@ -4,8 +4,8 @@ Argument marshalling only: every step of the computation runs in the library's
 gfx950 HIP kernels.  PyTorch supplies device memory and the current HIP stream.
 The entry points keep the C names:
 
-    quantize_qk_int8, sparse_attn_route, sparse_attn_fwd, gather_virtual_kv,
-    kv_cache_append_int8
+    quantize_qk_int8, sparse_attn_route, sparse_attn_fwd, sparse_attn_fwd_float,
+    gather_virtual_kv, kv_cache_append_int8
 
 plus ``sparse_attention`` which chains quantize -> route -> fwd.
 
@@ -23,7 +23,7 @@ from typing import Optional, Sequence
 
 import torch
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 SA_OK, SA_E_NULL, SA_E_SHAPE, SA_E_ALIGN, SA_E_VALUE, SA_E_UNSUPPORTED, SA_E_DEVICE, SA_E_LAUNCH, SA_E_WORKSPACE = range(9)
 SA_DROP, SA_EXACT, SA_CENTROID = 0, 1, 2
 SA_BF16, SA_INT8, SA_F32 = 0, 1, 2
@@ -100,6 +100,9 @@ def load(path: Optional[str] = None):
     lib.gather_virtual_kv.restype = i32
     lib.kv_cache_append_int8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, i32, i32, vp]
     lib.kv_cache_append_int8.restype = i32
+    lib.sparse_attn_fwd_float.argtypes = [vp, vp, vp, vp, P(sa_dims), P(sa_route_params), vp, vp, vp, vp, f32, vp,
+                                          i32, vp, vp]
+    lib.sparse_attn_fwd_float.restype = i32
     if path is None:
         _LIB = lib
     return lib
@@ -318,6 +321,48 @@ def sparse_attn_fwd(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k
                                   _ptr(v_block_src), ctypes.byref(dims), ctypes.byref(prm), _ptr(block_map),
                                   _ptr(k_centroid), _ptr(v_centroid), _ptr(count), float(sm), _ptr(out), odt,
                                   _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def sparse_attn_fwd_float(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_map: torch.Tensor, *,
+                          k_centroid=None, v_centroid=None, count=None, lq_valid: Optional[int] = None,
+                          lkv_valid: Optional[int] = None, v_block_src: Optional[torch.Tensor] = None,
+                          centroids_per_block: int = 1, kblock: int = 64, sm_scale: Optional[float] = None,
+                          out_dtype: torch.dtype = torch.float32, return_lse: bool = False,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, segments=None,
+                          stream=None):
+    """Forward with a floating QK^T on bf16 q [B,H,Lq,d], k [B,H,Lkv,d],
+    v [B,H,Lv,d]; map and centroids from sparse_attn_route."""
+    B, H, Lq, d = q.shape
+    Lkv, Lv = k.shape[2], v.shape[2]
+    lq_valid = Lq if lq_valid is None else lq_valid
+    lkv_valid = Lkv if lkv_valid is None else lkv_valid
+    G = centroids_per_block
+    nQB, nKB = Lq // 128, Lkv // kblock
+    _need(q, "q", torch.bfloat16, (B, H, Lq, d))
+    _need(k, "k", torch.bfloat16, (B, H, Lkv, d))
+    _need(v, "v", torch.bfloat16, (B, H, Lv, d))
+    if v_block_src is not None:
+        _need(v_block_src, "v_block_src", torch.int32, (Lkv // 64,))
+    _need(block_map, "block_map", torch.uint8, (B, H, nQB, nKB))
+    if G > 0:
+        _need(k_centroid, "k_centroid", torch.float32, (B, H, nKB, G, d))
+        _need(v_centroid, "v_centroid", torch.float32, (B, H, nKB, G, d))
+        _need(count, "count", torch.float32, (B, H, nKB, G))
+    odt = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=out_dtype, device=q.device)
+    _need(out, "out", out_dtype, (B, H, Lq, d))
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H, Lq))
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+    dims = _dims(B, H, Lq, Lkv, d, lq_valid, lkv_valid, Lv)
+    prm = _params(float("nan"), G, 0, kblock, kblock, 128, kblock, segments=segments)
+    _check(load().sparse_attn_fwd_float(_ptr(q), _ptr(k), _ptr(v), _ptr(v_block_src), ctypes.byref(dims),
+                                        ctypes.byref(prm), _ptr(block_map), _ptr(k_centroid), _ptr(v_centroid),
+                                        _ptr(count), float(sm), _ptr(out), odt, _ptr(lse), _stream(stream)))
     return (out, lse) if return_lse else out
 
 

@@ -315,6 +315,38 @@ int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k, 
   return launched(sa::launch_fwd(a, static_cast<hipStream_t>(stream)), "fwd");
 }
 
+int32_t sparse_attn_fwd_float(const void* q_bf16, const void* k_bf16, const void* v_bf16, const int32_t* v_block_src,
+                              const sa_dims* dims, const sa_route_params* p, const uint8_t* block_map,
+                              const float* k_centroid, const float* v_centroid, const float* count, float sm_scale,
+                              void* out, int32_t out_dtype, float* lse, void* stream) {
+  if (const int32_t rc = check_dims(dims, p, v_block_src != nullptr)) return rc;
+  sa::KvLayout lay;
+  if (const int32_t rc = build_layout(dims, p, &lay)) return rc;
+  if (!q_bf16 || !k_bf16 || !v_bf16 || !block_map || !out)
+    return fail(SA_E_NULL, "sparse_attn_fwd_float: q, k, v, block_map and out are required");
+  if (!aligned16(q_bf16) || !aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(out))
+    return fail(SA_E_ALIGN, "sparse_attn_fwd_float: q, k, v and out must be 16-byte aligned");
+  if (out_dtype != SA_F32 && out_dtype != SA_BF16) return fail(SA_E_VALUE, "sparse_attn_fwd_float: out_dtype must be SA_F32 or SA_BF16");
+  if (!(sm_scale > 0.0f) || isinf(sm_scale)) return fail(SA_E_VALUE, "sparse_attn_fwd_float: sm_scale must be positive and finite");
+  if (p->centroids_per_block > 0) {
+    if (!k_centroid || !v_centroid || !count) return fail(SA_E_NULL, "sparse_attn_fwd_float: centroids are required when G > 0");
+    if (!aligned16(k_centroid) || !aligned16(v_centroid)) return fail(SA_E_ALIGN, "sparse_attn_fwd_float: centroids must be 16-byte aligned");
+  }
+  if (dims->Lkv % p->kblock) return fail(SA_E_SHAPE, "sparse_attn_fwd_float: Lkv must be a multiple of kblock");
+  if ((int64_t)dims->B * dims->H * (dims->Lq / 128) > 0x7FFFFFFF) return fail(SA_E_SHAPE, "sparse_attn_fwd_float: too many query blocks");
+  if (const int32_t rc = check_current_device()) return rc;
+  if (dims->Lq == 0) return ok();
+  sa::FwdFloatArgs a{};
+  a.q = static_cast<const uint16_t*>(q_bf16); a.k = static_cast<const uint16_t*>(k_bf16);
+  a.v = static_cast<const uint16_t*>(v_bf16); a.v_block_src = v_block_src;
+  a.map = block_map; a.kc = k_centroid; a.vc = v_centroid; a.cnt = count; a.out = out; a.lse = lse;
+  a.B = dims->B; a.H = dims->H; a.Lq = dims->Lq; a.Lkv = dims->Lkv; a.Lv = dims->Lv; a.d = dims->d;
+  a.lq_valid = dims->lq_valid; a.lkv_valid = dims->lkv_valid;
+  a.nQB = dims->Lq / 128; a.nKB = dims->Lkv / p->kblock; a.kblock = p->kblock; a.G = p->centroids_per_block;
+  a.lay = lay; a.out_bf16 = out_dtype == SA_BF16; a.sm_log2 = sm_scale * 1.4426950408889634f;
+  return launched(sa::launch_fwd_float(a, static_cast<hipStream_t>(stream)), "fwd_float");
+}
+
 int32_t gather_virtual_kv(const void* k_phys_bf16, int32_t B, int32_t H, int32_t rows_per_slice, int32_t n_phys,
                           int32_t d, const int32_t* src_map_host, int32_t n_logical, const float* rope_cos,
                           const float* rope_sin, int32_t rot_offset, int32_t d_rot, int32_t k_rows_per_block,

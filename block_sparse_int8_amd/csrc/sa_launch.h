@@ -114,7 +114,27 @@ struct FwdArgs {
   float sm_log2;   // sm_scale * log2(e)
 };
 
+// Forward with a floating QK^T: bf16 Q [B,H,Lq,d], K [B,H,Lkv,d], V [B,H,Lv,d].
+struct FwdFloatArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* v_block_src;
+  const uint8_t* map;
+  const float* kc;
+  const float* vc;
+  const float* cnt;
+  void* out;
+  float* lse;
+  int B, H, Lq, Lkv, Lv, d, lq_valid, lkv_valid;
+  int nQB, nKB, kblock, G;
+  KvLayout lay;
+  bool out_bf16;
+  float sm_log2;   // sm_scale * log2(e)
+};
+
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
+hipError_t launch_fwd_float(const FwdFloatArgs& a, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 4
+#define SA_ABI_VERSION 5
 
 enum sa_status {
   SA_OK = 0,
@@ -256,6 +256,24 @@ int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k,
                         const uint8_t* block_map, const float* k_centroid, const float* v_centroid,
                         const float* count, float sm_scale, void* out, int32_t out_dtype, float* lse,
                         void* stream);
+
+/* Forward pass with a floating QK^T (Configure Sol Sparse Attention, "How it
+ * works": with a floating dense backend the kept blocks are computed in
+ * floating point rather than on the W8A8 path; the block map and centroids
+ * are the same, routed on the INT8 codes).  As sparse_attn_fwd, except:
+ *   exact keys u:       logit = sm_scale * (q_t . k_u)       on the bf16 values
+ *   centroid groups g:  logit = sm_scale * (q_t . kbar_g) + ln(n_g)
+ * with q_t the bf16 query (fp32 accumulation of bf16 products).
+ *   q_bf16  bf16 [B,H,Lq,d], k_bf16 bf16 [B,H,Lkv,d], v_bf16 bf16 [B,H,Lv,d],
+ *           dense; v_block_src as for sparse_attn_fwd
+ *   p       kblock, centroids_per_block and the key layout are used
+ *   block_map, k_centroid, v_centroid, count, sm_scale, out, out_dtype, lse:
+ *           as for sparse_attn_fwd */
+int32_t sparse_attn_fwd_float(const void* q_bf16, const void* k_bf16, const void* v_bf16,
+                              const int32_t* v_block_src, const sa_dims* dims, const sa_route_params* p,
+                              const uint8_t* block_map, const float* k_centroid, const float* v_centroid,
+                              const float* count, float sm_scale, void* out, int32_t out_dtype, float* lse,
+                              void* stream);
 
 /* Virtual-KV gather, "fast" mode (Configure H3 Static Virtual KV, mode list):
  * logical slice l (of n_logical, at most 16) re-reads physical slice

@@ -58,12 +58,19 @@ def gpu_pipeline(wl, tau=None, out_dtype=torch.float32, kblock=None, map_kblock=
                              v_scale_rows=wl.v_scale_rows, explicit_map=em,
                              map_kblock=map_kblock or wl.map_kblock, rule=wl.rule, sparsity=wl.sparsity,
                              segments=wl.segments, row_stats=True)
-    out, lse = sa.sparse_attn_fwd(q8, qs, k8, ks, v_in, r["map"], k_centroid=r["k_centroid"],
-                                  v_centroid=r["v_centroid"], count=r["count"], lq_valid=wl.lq_valid,
-                                  lkv_valid=wl.lkv_valid, v_scale=vsc, v_block_src=vbs, centroids_per_block=G,
-                                  kblock=kblock, k_scale_rows=wl.k_scale_rows, v_scale_rows=wl.v_scale_rows,
-                                  sm_scale=wl.sm_scale, out_dtype=out_dtype, return_lse=True,
-                                  segments=wl.segments)
+    if wl.qk_float:
+        out, lse = sa.sparse_attn_fwd_float(q, k, v, r["map"], k_centroid=r["k_centroid"],
+                                            v_centroid=r["v_centroid"], count=r["count"], lq_valid=wl.lq_valid,
+                                            lkv_valid=wl.lkv_valid, centroids_per_block=G, kblock=kblock,
+                                            sm_scale=wl.sm_scale, out_dtype=out_dtype, return_lse=True,
+                                            segments=wl.segments)
+    else:
+        out, lse = sa.sparse_attn_fwd(q8, qs, k8, ks, v_in, r["map"], k_centroid=r["k_centroid"],
+                                      v_centroid=r["v_centroid"], count=r["count"], lq_valid=wl.lq_valid,
+                                      lkv_valid=wl.lkv_valid, v_scale=vsc, v_block_src=vbs, centroids_per_block=G,
+                                      kblock=kblock, k_scale_rows=wl.k_scale_rows, v_scale_rows=wl.v_scale_rows,
+                                      sm_scale=wl.sm_scale, out_dtype=out_dtype, return_lse=True,
+                                      segments=wl.segments)
     torch.cuda.synchronize()
     host = lambda t: None if t is None else t.cpu().numpy()
     res = dict(q8=host(q8), q_scale=host(qs), k8=host(k8), k_scale=host(ks), map=host(r["map"]),

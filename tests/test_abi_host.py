@@ -26,6 +26,7 @@ def _declared_functions():
 def test_header_declares_the_four_calls():
     names = _declared_functions()
     for n in ("quantize_qk_int8", "sparse_attn_route", "sparse_attn_fwd", "gather_virtual_kv", "kv_cache_append_int8",
+              "sparse_attn_fwd_float",
               "sa_abi_version", "sa_last_error", "sa_device_check", "sparse_attn_route_workspace_size"):
         assert n in names, n
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 4
+    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 5
 
 
 def test_missing_library_lists_search_paths(monkeypatch, tmp_path):
@@ -220,3 +221,18 @@ def test_cache_append_validation():
     assert call(valid=300) == sa.SA_E_SHAPE
     assert call(d=96) == sa.SA_E_SHAPE
     assert lib.kv_cache_append_int8(None, 0, 0, 128, 1, 1, 256, 128, 256, 128, p, p, 4, 0, None) == sa.SA_E_NULL
+
+
+def test_fwd_float_validation():
+    lib = _lib()
+    p = ctypes.c_void_p(256)
+    dims, prm = _dims(), _prm()
+    call = lambda **kw: lib.sparse_attn_fwd_float(kw.get("q", p), p, p, None, ctypes.byref(kw.get("dims", dims)),
+                                                  ctypes.byref(kw.get("prm", prm)), p, p, p, p, kw.get("sm", 0.088), p,
+                                                  kw.get("odt", sa.SA_F32), None, None)
+    assert call(q=None) == sa.SA_E_NULL
+    assert call(q=ctypes.c_void_p(8)) == sa.SA_E_ALIGN
+    assert call(sm=0.0) == sa.SA_E_VALUE
+    assert call(odt=sa.SA_INT8) == sa.SA_E_VALUE
+    assert call(dims=_dims(d=96)) == sa.SA_E_SHAPE
+    assert call(prm=_prm(segments=[(0, 64, 0), (100, 10, 1)])) == sa.SA_E_VALUE

@@ -106,3 +106,10 @@ def test_full_ref2va_segments(sa, orc):
     nQB = wl.Lq // 128
     sel = np.unique(np.concatenate([sel, np.array(seg_q, dtype=np.int64), (wl.H - 1) * nQB + np.array(seg_q)]))
     _check_workload(orc, wl, sel=sel)
+
+
+def test_full_wan14b_like_float_qk(sa, orc):
+    """The 32K workload with the floating QK path (sampled query blocks)."""
+    wl = W.config(3)
+    wl.qk_float = True
+    _check_workload(orc, wl, sel=_sample(wl, 8, 9, frame_tokens=30 * 52))

@@ -290,3 +290,31 @@ def test_segmented_layout_topk(sa, orc, G):
     wl.centroids_per_block = G
     wl.rule, wl.sparsity = 1, 0.75
     _check_workload(orc, wl)
+
+
+@pytest.mark.parametrize("d,G,kblock,valid", [(128, 1, 64, 1000), (64, 1, 64, 1024), (128, 2, 64, 1000),
+                                              (128, 1, 128, 1000)])
+def test_float_qk_forward(sa, orc, d, G, kblock, valid):
+    """Floating QK^T on the bf16 Q/K for the exact tiles; same map and
+    centroids as the INT8 path."""
+    wl = W.tiny_sol(seed=51, H=2, L=1024, d=d, valid=valid, centroids_per_block=G)
+    wl.kblock = wl.k_scale_rows = kblock
+    wl.qk_float = True
+    _check_workload(orc, wl, tau=0.5)
+
+
+def test_float_qk_prefix_and_segments(sa, orc):
+    wl = W.config(4, small=True)
+    wl.qk_float = True
+    _check_workload(orc, wl)
+    wl = _segmented(centroids_per_block=2)
+    wl.qk_float = True
+    _check_workload(orc, wl)
+
+
+def test_float_qk_explicit_map_no_centroids(sa, orc):
+    """The LCSA pattern over bf16 K/V (G = 0)."""
+    wl = W.config(2, small=True)
+    wl.v_int8 = False
+    wl.qk_float = True
+    _check_workload(orc, wl)
