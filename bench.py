@@ -97,7 +97,8 @@ def cpu_baseline(wl, sample_stride: int):
     sel = np.arange(0, total, sample_stride, dtype=np.int64)
     out, lse, _ = oracle.forward(q8, qs, k8, ks, 64, wl.lq_valid, wl.lkv_valid, r["map"], kbar=r["kbar"],
                                  vbar=r["vbar"], count=r["count"], v_bits=wl.v, kblock=64, G=1,
-                                 sm_scale=wl.sm_scale, sel=sel)
+                                 sm_scale=wl.sm_scale, sel=sel, q_bits=wl.q if wl.qk_float else None,
+                                 k_bits=wl.k if wl.qk_float else None)
     t3 = time.perf_counter()
     fwd_full = (t3 - t2) * total / len(sel)
     est = (t1 - t0) + (t2 - t1) + fwd_full
@@ -174,6 +175,8 @@ def main():
     ap.add_argument("--rule", choices=["threshold", "topk"], default="threshold",
                     help="routing rule: Sol threshold 1.0 (the measured workload) or fixed sparsity")
     ap.add_argument("--sparsity", type=float, default=0.75, help="pruned fraction for --rule topk")
+    ap.add_argument("--qk-float", action="store_true",
+                    help="exact tiles on the floating path (bf16 QK^T) instead of INT8 (same map and centroids)")
     ap.add_argument("--cache-append", action="store_true",
                     help="measure the streaming INT8 K/V cache append instead (FlashVSR-like: H=12, frames of "
                          "2048 rows, a ring of four frames)")
@@ -198,6 +201,7 @@ def main():
     topk = args.rule == "topk"
     if topk:
         wl.rule, wl.sparsity = 1, args.sparsity
+    wl.qk_float = args.qk_float
     log(f"[bench] generated {wl.name}: B={wl.B} H={wl.H} L={wl.Lq} d={wl.d} in {time.perf_counter() - t:.1f}s")
     q, k, v = bf16_dev(wl.q), bf16_dev(wl.k), bf16_dev(wl.v)
     B, H, L, d = q.shape
@@ -228,10 +232,16 @@ def main():
                                  rule=wl.rule, sparsity=wl.sparsity, outputs=routed)
         ws = r["workspace"]
         if ev: ev[3].record(stream)
-        sa.sparse_attn_fwd(q8, qs, k8, ks, v, routed["map"], k_centroid=routed["k_centroid"],
-                           v_centroid=routed["v_centroid"], count=routed["count"], lq_valid=wl.lq_valid,
-                           lkv_valid=wl.lkv_valid, centroids_per_block=1, kblock=64, sm_scale=wl.sm_scale,
-                           out_dtype=torch.bfloat16, out=out)
+        if args.qk_float:
+            sa.sparse_attn_fwd_float(q, k, v, routed["map"], k_centroid=routed["k_centroid"],
+                                     v_centroid=routed["v_centroid"], count=routed["count"], lq_valid=wl.lq_valid,
+                                     lkv_valid=wl.lkv_valid, centroids_per_block=1, kblock=64,
+                                     sm_scale=wl.sm_scale, out_dtype=torch.bfloat16, out=out)
+        else:
+            sa.sparse_attn_fwd(q8, qs, k8, ks, v, routed["map"], k_centroid=routed["k_centroid"],
+                               v_centroid=routed["v_centroid"], count=routed["count"], lq_valid=wl.lq_valid,
+                               lkv_valid=wl.lkv_valid, centroids_per_block=1, kblock=64, sm_scale=wl.sm_scale,
+                               out_dtype=torch.bfloat16, out=out)
         if ev: ev[4].record(stream)
 
     if args.calibrate_copy_mib:
@@ -266,8 +276,10 @@ def main():
     # The exact tiles do as many int8 ops (QK^T) as bf16 flops (PV), so the
     # kernel's ceiling is the harmonic combination of the two peaks.
     peak_mixed = 1.0 / (0.5 / PEAK_INT8 + 0.5 / PEAK_BF16)
+    if args.qk_float:
+        peak_mixed = PEAK_BF16   # both products on bf16 matrix cores
     khash = kernel_hash()
-    traffic = read_traffic(khash)
+    traffic = None if args.qk_float else read_traffic(khash)   # counters were taken on the INT8 kernel
     elems = B * H * L * d
     quant_bytes = elems * 2 + elems * 1 + B * H * nQB * 4
     dense_ops = 4.0 * B * H * L * L * d
@@ -276,7 +288,8 @@ def main():
     kept = float((bmap[..., :valid_blocks] == 1).mean())
     rule_desc = f"top-k sparsity {wl.sparsity:g}" if topk else f"threshold {wl.threshold:g}"
     res = {
-        "metric": METRIC if not topk else METRIC.replace("thr=1.0", f"top-k sparsity={wl.sparsity:g}"),
+        "metric": (METRIC if not topk else METRIC.replace("thr=1.0", f"top-k sparsity={wl.sparsity:g}"))
+                  + (", bf16 QK" if args.qk_float else ""),
         "value": round(value, 3),
         "unit": "dense-equiv TOPS",
         "n_gpus": 1,
@@ -286,7 +299,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 QK^T + fp32 softmax + bf16 PV",
+        "dtype": "bf16 QK^T + fp32 softmax + bf16 PV" if args.qk_float else "int8 QK^T + fp32 softmax + bf16 PV",
         "data": "synthetic (seeded per-frame low-rank correlated bf16 Q/K/V)",
         "config": {"workload": f"Wan-14B-like Sol 1x64: B=1 H={H} d=128 L=32768 (32760 valid), {rule_desc}",
                    "B": B, "H": H, "L": L, "d": d, "valid": wl.lkv_valid, "kblock": 64, "centroids": "1x64",
@@ -298,7 +311,8 @@ def main():
                     "map_entries": int(bmap.size)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak_mixed, 2),
                      "unit": "TFLOP/s", "frac": round(achieved / peak_mixed, 4), "traffic": traffic,
-                     "kernel": "sparse_attn_fwd (fwd_kernel<128,false,true>)",
+                     "kernel": ("sparse_attn_fwd_float (fwd_float_kernel<128,true>)" if args.qk_float
+                                else "sparse_attn_fwd (fwd_kernel<128,false,true>)"),
                      "frac_of_int8_peak": round(achieved / PEAK_INT8, 4), "kernel_hash": khash},
         "hbm_kernels": {
             "quantize_qk_int8": {"bytes": quant_bytes,

@@ -11,10 +11,11 @@
 // in the operand layout the PV product takes; O^T += V^T.P^T with V^T read by
 // ds_read_b64_tr_b16; centroid columns 32 at a time in the same softmax.
 // Differences: S^T on v_mfma_f32_32x32x16_bf16 (D/16 k-steps per half) from a
-// bf16 K tile, scores straight in fp32, a plain max-then-weights step per half,
-// and tile copies staged through registers: the next tile's global loads are
-// issued before the current tile's compute and written to the other LDS stage
-// after it.
+// bf16 K tile, scores straight in fp32 (the weights use the INT8 kernel's fast
+// path against a lagging running max, with the same hand interleaving of one
+// half's weights with the other half's matrix work), and tile copies straight
+// into LDS: the next tile's copy goes into the other stage while the current
+// tile is computed.
 #include "sa_device.h"
 #include "sa_launch.h"
 
@@ -33,9 +34,9 @@ struct FltLds {
   static constexpr int STAGE = V_OFF + kTile * VSTR;
   static constexpr int KCL_OFF = 32 * KSTR;   // centroid K lo rows (hi rows at 0), in stage 0
   static constexpr int VCL_OFF = 32 * VSTR;   // centroid V lo rows (hi rows at 0), in stage 1
-  static constexpr int TU = kTile * 2 * D / 16 / 256;   // 16-byte units per thread per tile (K or V)
   static_assert(2 * 32 * KSTR <= STAGE && 2 * 32 * VSTR <= STAGE, "centroid staging must fit a stage");
-  static_assert(TU * 256 * 16 == kTile * 2 * D, "a tile is a whole number of 16-byte units per thread");
+  static_assert(V_OFF % 1024 == 0 && (kTile * KSTR) % 1024 == 0 && (kTile * VSTR) % 1024 == 0,
+                "copy instructions write whole 1 KiB chunks");
 };
 
 __device__ __forceinline__ v4bf ftr16(const uint8_t* p) {
@@ -64,40 +65,80 @@ __device__ __forceinline__ void frescale(float m_tile, float& m_run, float& l_ru
   }
 }
 
-// One 64-key tile in registers: TU 16-byte units of K and of V per thread.
-template <int D>
-struct FltRegs {
-  uint4 k[FltLds<D>::TU], v[FltLds<D>::TU];
-};
+// Tile copies straight into LDS (buffer_load_dwordx4 ... lds): lane L of a
+// wave instruction writes LDS bytes 16L..16L+15 of that instruction's 1 KiB
+// chunk, so the padded row layout comes from each lane's source offset; lanes
+// on padding read past the buffer (zeros, no memory access).  Instruction u
+// of a tile belongs to wave u % 4.  The LDS address is handed over as a
+// wave-uniform integer the compiler cannot trace to an LDS variable, so it
+// adds no wait of its own before later LDS reads; the tile loop's barriers
+// wait for the copies.  Kept out of templates (the host pass only accepts the
+// builtin in a plain function).
+constexpr uint32_t kFPad = 0xFFFFFFF0u;
 
-// Global loads of tile kt (64 logical key rows from krow0; V rows from vrow0).
-template <int D>
-__device__ __forceinline__ void flt_load(const uint16_t* kbase, const uint16_t* vbase, int krow0, int vrow0,
-                                         FltRegs<D>& r, int tid) {
-  constexpr int UPR = 2 * D / 16;   // 16-byte units per row
-#pragma unroll
-  for (int e = 0; e < FltLds<D>::TU; ++e) {
-    const int u = tid + 256 * e, row = u / UPR, c = u % UPR;
-    r.k[e] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(krow0 + row) * D + c * 8);
-    r.v[e] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(vrow0 + row) * D + c * 8);
-  }
+__device__ __forceinline__ void flt_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                          uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("" : "+s"(lds_addr));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SA_LDS void*)(uintptr_t)lds_addr, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t flt_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
 }
 
 template <int D>
-__device__ __forceinline__ void flt_store(uint8_t* stage, const FltRegs<D>& r, int tid) {
-  using L = FltLds<D>;
-  constexpr int UPR = 2 * D / 16;
+struct FltPlan {
+  static constexpr int KU = FltLds<D>::KSTR / 16, VU = FltLds<D>::VSTR / 16;   // 16-byte units per row
+  static constexpr int KN = kTile * KU / 64, VN = kTile * VU / 64;               // wave instructions per tile
+  static constexpr int KI = (KN + 3) / 4, VI = (VN + 3) / 4;                     // per wave (at most)
+  uint32_t koff[KI], voff[VI];
+};
+
+template <int D>
+__device__ __forceinline__ FltPlan<D> flt_plan(int wave, int lane) {
+  using P = FltPlan<D>;
+  P pl;
 #pragma unroll
-  for (int e = 0; e < L::TU; ++e) {
-    const int u = tid + 256 * e, row = u / UPR, c = u % UPR;
-    *reinterpret_cast<uint4*>(stage + row * L::KSTR + c * 16) = r.k[e];
-    *reinterpret_cast<uint4*>(stage + L::V_OFF + row * L::VSTR + c * 16) = r.v[e];
+  for (int t = 0; t < P::KI; ++t) {
+    const int u = (wave + 4 * t) * 64 + lane, row = u / P::KU, cc = u % P::KU;
+    pl.koff[t] = cc < 2 * D / 16 ? (uint32_t)(row * 2 * D + cc * 16) : kFPad;
   }
+#pragma unroll
+  for (int t = 0; t < P::VI; ++t) {
+    const int u = (wave + 4 * t) * 64 + lane, row = u / P::VU, cc = u % P::VU;
+    pl.voff[t] = cc < 2 * D / 16 ? (uint32_t)(row * 2 * D + cc * 16) : kFPad;
+  }
+  return pl;
+}
+
+// Issue this wave's share of the copy of a tile (K rows from krow0, V rows
+// from vrow0) into stage.
+template <int D>
+__device__ __forceinline__ void flt_copy(const FltPlan<D>& pl, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                         int krow0, int vrow0, uint8_t* stage, int wave) {
+  using P = FltPlan<D>;
+  const uint32_t base = (uint32_t)(uintptr_t)(SA_LDS const void*)stage;
+#pragma unroll
+  for (int t = 0; t < P::KI; ++t)
+    if (wave + 4 * t < P::KN) flt_dma16(krs, pl.koff[t], (uint32_t)krow0 * 2 * D, base + (wave + 4 * t) * 1024);
+#pragma unroll
+  for (int t = 0; t < P::VI; ++t)
+    if (wave + 4 * t < P::VN)
+      flt_dma16(vrs, pl.voff[t], (uint32_t)vrow0 * 2 * D, base + FltLds<D>::V_OFF + (wave + 4 * t) * 1024);
+}
+
+// Wait for this wave's copies into LDS, then the workgroup barrier: after it
+// every copy issued before it has landed.
+__device__ __forceinline__ void flt_copies_done_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 // Physical first row of V for logical 64-row key tile kt.
 __device__ __forceinline__ int flt_vrow(const FwdFloatArgs& a, int kt) {
-  return a.v_block_src ? min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile : kt * kTile;
+  return a.v_block_src ? __builtin_amdgcn_readfirstlane(min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile)
+                       : kt * kTile;
 }
 
 // O^T += V^T.P^T for one 32-key half (keys key0..key0+31 of the staged tile).
@@ -152,25 +193,92 @@ __device__ __forceinline__ float flt_half_softmax(const v16f& acc, int key0, flo
   return psum;
 }
 
+// Fast-path acceptance bound on a lane's partial row sum (weights taken against
+// a running max that lags the scores stay far from fp32/bf16 overflow).
+constexpr float kFFastSum = 4096.0f;
+
+__device__ __forceinline__ bool flt_fast_ok(float psum) { return __ballot(!(psum <= kFFastSum)) == 0; }
+
+// Weights 2e, 2e+1 of a half against the current m (b = -m): two FMAs, two
+// exp2, one bf16 pack and the row-sum update.
+__device__ __forceinline__ void flt_weight_pair(const v16f& acc, int e, float c, float b, float& psum,
+                                                uint32_t (&pw)[8]) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[2 * e], c, b));
+  const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[2 * e + 1], c, b));
+  const v2bf pk = (v2bf){(__bf16)p0, (__bf16)p1};
+  psum = __builtin_amdgcn_fdot2_f32_bf16(pk, (v2bf){(__bf16)1.0f, (__bf16)1.0f}, psum, false);
+  pw[e] = __builtin_bit_cast(uint32_t, pk);
+}
+
 // One staged 64-key tile (keys >= nvalid masked when MASKED).
+//   Full tiles: each half's weights are first taken against m_run as it
+//   stands and kept when every lane's partial row sum is finite and at most
+//   kFFastSum, else recomputed after moving m_run (the first tile, a jump in
+//   the scores).  A wave issues in order, so the weights of half 0 are placed
+//   between the QK MFMAs of half 1 and those of half 1 between the PV MFMAs
+//   of half 0, in fixed scheduling segments.
+//   Masked tiles: max, rescale and weights per half.
 template <int D, bool MASKED>
 __device__ __forceinline__ void flt_tile(const uint8_t* buf, const v8bf (&qf)[D / 16], v16f (&O)[D / 32],
                                          float& m_run, float& l_run, float c, int nvalid, int klane, int vlane,
                                          int hh) {
   using L = FltLds<D>;
   constexpr int NS = D / 32, KS = D / 16;
+  const uint8_t* vbuf = buf + L::V_OFF;
+  v16f acc0 = (v16f){}, acc1 = (v16f){};
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    v16f acc = (v16f){};
+  for (int s = 0; s < KS; ++s)
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const v8bf*>(buf + klane + s * 32), qf[s], acc0,
+                                                   0, 0, 0);
+  uint32_t pw0[8], pw1[8];
+  if (MASKED) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const v8bf*>(buf + klane + 32 * L::KSTR + s * 32), qf[s], acc1, 0, 0, 0);
+    l_run += flt_half_softmax<NS, true>(acc0, 0, c, nvalid, hh, O, m_run, l_run, pw0);
+    flt_half_pv<D>(vbuf, 0, pw0, O, vlane);
+    l_run += flt_half_softmax<NS, true>(acc1, 32, c, nvalid, hh, O, m_run, l_run, pw1);
+    flt_half_pv<D>(vbuf, 32, pw1, O, vlane);
+    return;
+  }
+  // QK of half 1, interleaved with the weights of half 0
+  float ps0 = 0.0f;
+  {
+    const float b = -m_run;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const v8bf kf = *reinterpret_cast<const v8bf*>(buf + klane + h * 32 * L::KSTR + s * 32);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const v8bf*>(buf + klane + 32 * L::KSTR + s * 32), qf[s], acc1, 0, 0, 0);
+#pragma unroll
+      for (int e = s * 8 / KS; e < (s + 1) * 8 / KS; ++e) flt_weight_pair(acc0, e, c, b, ps0, pw0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    uint32_t pw[8];
-    l_run += flt_half_softmax<NS, MASKED>(acc, h * 32, c, nvalid, hh, O, m_run, l_run, pw);
-    flt_half_pv<D>(buf + L::V_OFF, h * 32, pw, O, vlane);
   }
+  if (!flt_fast_ok(ps0)) ps0 = flt_half_softmax<NS, false>(acc0, 0, c, kTile, hh, O, m_run, l_run, pw0);
+  l_run += ps0;
+  // PV of half 0, interleaved with the weights of half 1
+  float ps1 = 0.0f;
+  {
+    const float b = -m_run;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NS; ++i) {
+      const uint8_t* p0 = vbuf + vlane + ((i / NS) * 16) * L::VSTR + (i % NS) * 64;
+      const int k2 = i / NS;
+      const v4i pwv = (v4i){(int)pw0[k2 * 4], (int)pw0[k2 * 4 + 1], (int)pw0[k2 * 4 + 2], (int)pw0[k2 * 4 + 3]};
+      O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fcat8(ftr16(p0), ftr16(p0 + 8 * L::VSTR)),
+                                                           __builtin_bit_cast(v8bf, pwv), O[i % NS], 0, 0, 0);
+#pragma unroll
+      for (int e = i * 8 / (2 * NS); e < (i + 1) * 8 / (2 * NS); ++e) flt_weight_pair(acc1, e, c, b, ps1, pw1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (!flt_fast_ok(ps1)) ps1 = flt_half_softmax<NS, false>(acc1, 32, c, kTile, hh, O, m_run, l_run, pw1);
+  l_run += ps1;
+  flt_half_pv<D>(vbuf, 32, pw1, O, vlane);
 }
 
 }  // namespace
@@ -214,9 +322,12 @@ __global__ __launch_bounds__(256, 2) void fwd_float_kernel(FwdFloatArgs a) {
   for (int cc = 0; cc < NS; ++cc) O[cc] = (v16f){};
   float m_run = -INFINITY, l_run = 0.0f;
   const uint8_t* mrow = a.map + (bh * a.nQB + i) * a.nKB;
-  const uint16_t* kbase = a.k + bh * a.Lkv * D;
-  const uint16_t* vbase = a.v + bh * a.Lv * D;
-  FltRegs<D> rg;
+  // buffer resources over this head's K and V (per-head sizes fit 32 bits:
+  // checked when the call is validated)
+  const __amdgpu_buffer_rsrc_t krs = flt_rsrc(a.k + bh * a.Lkv * D, (uint32_t)((int64_t)a.Lkv * D * 2));
+  const __amdgpu_buffer_rsrc_t vrs = flt_rsrc(a.v + bh * a.Lv * D, (uint32_t)((int64_t)a.Lv * D * 2));
+  const FltPlan<D> plan = flt_plan<D>(wave, lane);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform copy of the wave index
 
   for (int w0 = 0; w0 < a.nKB; w0 += kFWin) {
     const int wend = min(a.nKB, w0 + kFWin);
@@ -261,30 +372,26 @@ __global__ __launch_bounds__(256, 2) void fwd_float_kernel(FwdFloatArgs a) {
     // ---------------- full exact tiles, two stages ----------------
     if (nE > 0) {
       {
-        const int kt = w0 * tpb + elist[0];
-        flt_load<D>(kbase, vbase, kt * kTile, flt_vrow(a, kt), rg, tid);
-        flt_store<D>(stage0, rg, tid);
+        const int kt = __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]);
+        flt_copy<D>(plan, krs, vrs, kt * kTile, flt_vrow(a, kt), stage0, wave_u);
       }
-      __syncthreads();
+      flt_copies_done_barrier();
       for (int e = 0; e < nE; ++e) {
         uint8_t* cur = (e & 1) ? stage1 : stage0;
         uint8_t* nxt = (e & 1) ? stage0 : stage1;
-        const bool more = e + 1 < nE;
-        if (more) {
-          const int kt = w0 * tpb + elist[e + 1];
-          flt_load<D>(kbase, vbase, kt * kTile, flt_vrow(a, kt), rg, tid);   // in flight during the compute
+        if (e + 1 < nE) {   // next tile into the other stage, in flight during the compute
+          const int kt = __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 1]);
+          flt_copy<D>(plan, krs, vrs, kt * kTile, flt_vrow(a, kt), nxt, wave_u);
         }
         flt_tile<D, false>(cur, qf, O, m_run, l_run, c, kTile, klane, vlane, hh);
-        if (more) flt_store<D>(nxt, rg, tid);
-        __syncthreads();
+        flt_copies_done_barrier();
       }
     }
     // ---------------- tiles with the end of a segment's valid keys ----------------
     for (int pi = 0; pi < nP; ++pi) {
-      const int kt = plist[pi], nvalid = pvalid[pi];
-      flt_load<D>(kbase, vbase, kt * kTile, flt_vrow(a, kt), rg, tid);
-      flt_store<D>(stage0, rg, tid);
-      __syncthreads();
+      const int kt = __builtin_amdgcn_readfirstlane(plist[pi]), nvalid = pvalid[pi];
+      flt_copy<D>(plan, krs, vrs, kt * kTile, flt_vrow(a, kt), stage0, wave_u);
+      flt_copies_done_barrier();
       flt_tile<D, true>(stage0, qf, O, m_run, l_run, c, nvalid, klane, vlane, hh);
       __syncthreads();
     }
