@@ -318,3 +318,25 @@ def test_float_qk_explicit_map_no_centroids(sa, orc):
     wl.v_int8 = False
     wl.qk_float = True
     _check_workload(orc, wl)
+
+
+def test_float_qk_and_topk_degenerate(sa, orc):
+    """Nothing valid on the floating path; a single valid key (floating path,
+    and the fixed-sparsity rule with one candidate, floor(0.75) = 0 pruned);
+    a sparsity that prunes all but one of five candidates."""
+    wl = W.tiny_sol(seed=5, H=1, L=256, d=64, valid=0)
+    wl.qk_float = True
+    g = gpu_pipeline(wl)
+    assert not g["out"].any() and np.isneginf(g["lse"]).all()
+    wl = W.tiny_sol(seed=6, H=1, L=256, d=64)
+    wl.lkv_valid = 1
+    wl.qk_float = True
+    _check_workload(orc, wl)
+    wl = W.tiny_sol(seed=6, H=1, L=256, d=64)
+    wl.lkv_valid = 1
+    wl.rule, wl.sparsity = 1, 0.75
+    _check_workload(orc, wl)
+    wl = W.tiny_sol(seed=7, H=2, L=512, d=128, valid=300)
+    wl.rule, wl.sparsity = 1, 0.99
+    g, o = _check_workload(orc, wl)
+    assert ((g["map"][..., :5] == 1).sum(-1) == 1).all()
