@@ -138,6 +138,15 @@ int32_t build_layout(const sa_dims* dm, const sa_route_params* p, sa::KvLayout* 
   return SA_OK;
 }
 
+// The forward kernels address one head's K and V through 32-bit buffer
+// offsets: each must stay below 4 GiB.
+int32_t check_head_bytes(const sa_dims* dm, int k_bytes_per_elt, int v_bytes_per_elt, const char* who) {
+  const int64_t kb = (int64_t)dm->Lkv * dm->d * k_bytes_per_elt, vb = (int64_t)dm->Lv * dm->d * v_bytes_per_elt;
+  if (kb >= (int64_t)1 << 32 || vb >= (int64_t)1 << 32)
+    return fail(SA_E_SHAPE, "%s: one head's K or V exceeds 4 GiB (%lld, %lld bytes)", who, (long long)kb, (long long)vb);
+  return SA_OK;
+}
+
 int32_t check_v(int32_t v_dtype, const void* v, const float* v_scale, const sa_dims* dm, const sa_route_params* p) {
   if (v_dtype != SA_BF16 && v_dtype != SA_INT8) return fail(SA_E_VALUE, "v_dtype must be SA_BF16 or SA_INT8");
   if (!v) return fail(SA_E_NULL, "v must not be NULL");
@@ -299,6 +308,7 @@ int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k, 
     if (!aligned16(k_centroid) || !aligned16(v_centroid)) return fail(SA_E_ALIGN, "sparse_attn_fwd: centroids must be 16-byte aligned");
   }
   if (dims->Lkv % p->kblock) return fail(SA_E_SHAPE, "sparse_attn_fwd: Lkv must be a multiple of kblock");
+  if (const int32_t rc = check_head_bytes(dims, 1, v_dtype == SA_INT8 ? 1 : 2, "sparse_attn_fwd")) return rc;
   if (const int32_t rc = check_current_device()) return rc;
   if (dims->Lq == 0) return ok();
   sa::FwdArgs a{};
@@ -333,6 +343,7 @@ int32_t sparse_attn_fwd_float(const void* q_bf16, const void* k_bf16, const void
     if (!aligned16(k_centroid) || !aligned16(v_centroid)) return fail(SA_E_ALIGN, "sparse_attn_fwd_float: centroids must be 16-byte aligned");
   }
   if (dims->Lkv % p->kblock) return fail(SA_E_SHAPE, "sparse_attn_fwd_float: Lkv must be a multiple of kblock");
+  if (const int32_t rc = check_head_bytes(dims, 2, 2, "sparse_attn_fwd_float")) return rc;
   if ((int64_t)dims->B * dims->H * (dims->Lq / 128) > 0x7FFFFFFF) return fail(SA_E_SHAPE, "sparse_attn_fwd_float: too many query blocks");
   if (const int32_t rc = check_current_device()) return rc;
   if (dims->Lq == 0) return ok();

@@ -41,6 +41,8 @@
  *    would be without them).  Query rows inside the layout's padding are
  *    computed like any other row below lq_valid.
  *  - Only gfx950 devices are accepted; others give SA_E_UNSUPPORTED.
+ *  - The forward passes address one head's K and V with 32-bit offsets: each
+ *    must be below 4 GiB (SA_E_SHAPE otherwise).
  */
 #ifndef SPARSE_ATTN_H
 #define SPARSE_ATTN_H

@@ -236,3 +236,19 @@ def test_fwd_float_validation():
     assert call(odt=sa.SA_INT8) == sa.SA_E_VALUE
     assert call(dims=_dims(d=96)) == sa.SA_E_SHAPE
     assert call(prm=_prm(segments=[(0, 64, 0), (100, 10, 1)])) == sa.SA_E_VALUE
+
+
+def test_forward_rejects_heads_over_4gib():
+    """With a V block table, V may be longer than the key sequence; a head's
+    bf16 V of 2^24 rows x 256 B would overflow the kernels' 32-bit buffer
+    offsets, and both forwards refuse it before touching memory."""
+    lib = _lib()
+    p = ctypes.c_void_p(256)
+    big = _dims(Lq=256, Lkv=256, lkv_valid=256, Lv=1 << 24, d=128)
+    prm = _prm(centroids_per_block=0)
+    rc = lib.sparse_attn_fwd(p, p, p, p, p, sa.SA_BF16, None, p, ctypes.byref(big), ctypes.byref(prm), p, None,
+                             None, None, 0.088, p, sa.SA_F32, None, None)
+    assert rc == sa.SA_E_SHAPE and "4 GiB" in _err()
+    rc = lib.sparse_attn_fwd_float(p, p, p, p, ctypes.byref(big), ctypes.byref(prm), p, None, None, None, 0.088, p,
+                                   sa.SA_F32, None, None)
+    assert rc == sa.SA_E_SHAPE and "4 GiB" in _err()
