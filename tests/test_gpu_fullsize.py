@@ -113,3 +113,21 @@ def test_full_wan14b_like_float_qk(sa, orc):
     wl = W.config(3)
     wl.qk_float = True
     _check_workload(orc, wl, sel=_sample(wl, 8, 9, frame_tokens=30 * 52))
+
+
+def test_full_ref2va_segments_topk(sa, orc):
+    """The reference-conditioned layout under the fixed-sparsity rule (0.75, the
+    Ref2VA VSA recipe): only the routed video segments are pruned."""
+    wl = W.ref2va_segments()
+    wl.rule, wl.sparsity = 1, 0.75
+    g, o = _check_workload(orc, wl, sel=_sample(wl, 8, 10))
+    first_routed = int(wl.segments[3][0]) // 64
+    assert (g["map"][..., :first_routed] != 2).all()
+
+
+def test_full_flashvsr_lcsa_float_qk(sa, orc):
+    """FlashVSR's LCSA pattern on the floating QK path (bf16 K and V)."""
+    wl = W.config(2)
+    wl.v_int8 = False
+    wl.qk_float = True
+    _check_workload(orc, wl, sel=_sample(wl, 16, 11, frame_tokens=32 * 64))
