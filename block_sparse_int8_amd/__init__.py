@@ -136,6 +136,8 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, contiguous
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -176,6 +178,8 @@ def kv_cache_append_int8(x: torch.Tensor, cache_q: torch.Tensor, cache_scale: to
     B, H, rows, d = x.shape
     if x.stride(3) != 1:
         raise ValueError("x must have a contiguous channel dimension")
+    if cache_scale.dim() != 3:
+        raise ValueError("cache_scale must be [B,H,slots]")
     slots = cache_scale.shape[2]
     _need(cache_q, "cache_q", torch.int8, (B, H, slots * rows_per_slab, d))
     _need(cache_scale, "cache_scale", torch.float32, (B, H, slots))
