@@ -44,12 +44,12 @@ struct FwdLds {
   static constexpr int KCSTR = 2 * D + 16;    // bf16 centroid-K row stride (bytes)
   static constexpr int KU = KSTR / 16;        // 16-byte units per K row (last one padding)
   static constexpr int VU = VSTR / 16;        // 16-byte units per V row (last four padding)
-  static constexpr int V_OFF = kTile * KSTR;
-  static constexpr int STAGE = V_OFF + kTile * VSTR;   // one pipeline stage: K tile + V tile
-  // centroid staging: K hi/lo in stage 0, V hi/lo in stage 1
+  static constexpr int KST = kTile * KSTR;    // one K stage
+  static constexpr int VST = kTile * VSTR;    // one V stage
+  // centroid staging: K hi/lo in V stage 0, V hi/lo in V stage 1
   static constexpr int KCL_OFF = 32 * KCSTR;
   static constexpr int VCL_OFF = 32 * VSTR;
-  static_assert(2 * 32 * KCSTR <= STAGE && 2 * 32 * VSTR <= STAGE, "centroid staging must fit a stage");
+  static_assert(2 * 32 * KCSTR <= VST && 2 * 32 * VSTR <= VST, "centroid staging must fit a V stage");
 };
 
 __device__ __forceinline__ v4bf tr16(const uint8_t* lds_byte_ptr) {
@@ -121,6 +121,8 @@ struct DmaPlan {
 // the buffer load returns zeros for them without touching memory.
 constexpr uint32_t kPadOffset = 0xFFFFFFF0u;
 
+// Instruction slots past the end of a tile (when its instruction count is not
+// a multiple of 4) fetch nothing on every lane and land in a 1 KiB sink.
 template <int D>
 __device__ __forceinline__ DmaPlan<D> make_dma_plan(int wave, int lane) {
   using L = FwdLds<D>;
@@ -128,12 +130,12 @@ __device__ __forceinline__ DmaPlan<D> make_dma_plan(int wave, int lane) {
 #pragma unroll
   for (int t = 0; t < DmaPlan<D>::KI; ++t) {
     const int u = (wave + 4 * t) * 64 + lane, row = u / L::KU, c = u % L::KU;
-    pl.koff[t] = c < D / 16 ? (uint32_t)(row * D + c * 16) : kPadOffset;
+    pl.koff[t] = row < kTile && c < D / 16 ? (uint32_t)(row * D + c * 16) : kPadOffset;
   }
 #pragma unroll
   for (int t = 0; t < DmaPlan<D>::VI; ++t) {
     const int u = (wave + 4 * t) * 64 + lane, row = u / L::VU, c = u % L::VU;
-    pl.voff[t] = c < 2 * D / 16 ? (uint32_t)(row * 2 * D + c * 16) : kPadOffset;
+    pl.voff[t] = row < kTile && c < 2 * D / 16 ? (uint32_t)(row * 2 * D + c * 16) : kPadOffset;
   }
   return pl;
 }
@@ -155,13 +157,13 @@ __device__ __forceinline__ void load_v_int8(const int8_t* vsrc, VRegs<D>& vr, in
 }
 
 template <int D>
-__device__ __forceinline__ void store_v_int8(uint8_t* buf, const VRegs<D>& vr, int tid) {
+__device__ __forceinline__ void store_v_int8(uint8_t* vbuf, const VRegs<D>& vr, int tid) {
   using L = FwdLds<D>;
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) {
     const int v = tid + 256 * e, r = v / (D / 16), cc = v % (D / 16);
-    *reinterpret_cast<v8bf*>(buf + L::V_OFF + r * L::VSTR + cc * 32) = i8x8_to_bf16(vr.r[e][0], vr.r[e][1]);
-    *reinterpret_cast<v8bf*>(buf + L::V_OFF + r * L::VSTR + cc * 32 + 16) = i8x8_to_bf16(vr.r[e][2], vr.r[e][3]);
+    *reinterpret_cast<v8bf*>(vbuf + r * L::VSTR + cc * 32) = i8x8_to_bf16(vr.r[e][0], vr.r[e][1]);
+    *reinterpret_cast<v8bf*>(vbuf + r * L::VSTR + cc * 32 + 16) = i8x8_to_bf16(vr.r[e][2], vr.r[e][3]);
   }
 }
 
@@ -193,22 +195,24 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(SA_LDS const void*)p;
 }
 
-// Scalars of one exact tile, loaded when its copy is issued (before the direct
-// loads) so the compute of the previous tile never waits on them.
+// Scalars of one exact tile, loaded a tile or more before they are used, so
+// the compute never waits on them: the loads are consumed after a later
+// barrier (which waits for all of this wave's loads).
 struct TileInfo {
-  int krow0, vrow0;
-  float kscale, pscale;   // raw loads: consumed only after the next barrier
+  int krow0;
+  int vsrc;               // V row of the tile (raw load when V rows are remapped)
+  float kscale, pscale;
+  __device__ __forceinline__ int vrow0() const { return __builtin_amdgcn_readfirstlane(vsrc); }
 };
 
 template <bool VI8>
 __device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int kt, int nKS, int nVS) {
   TileInfo t;
   t.krow0 = kt * kTile;
-  t.vrow0 = t.krow0;
-  if (a.v_block_src)
-    t.vrow0 = __builtin_amdgcn_readfirstlane(min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile);
+  t.vsrc = a.v_block_src ? min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile : t.krow0;
+  if (VI8) t.vsrc = __builtin_amdgcn_readfirstlane(t.vsrc);   // the V scale index needs it now
   t.kscale = a.k_scale[bh * nKS + t.krow0 / a.k_scale_rows];
-  t.pscale = VI8 ? a.v_scale[bh * nVS + t.vrow0 / a.v_scale_rows] : 1.0f;
+  t.pscale = VI8 ? a.v_scale[bh * nVS + t.vsrc / a.v_scale_rows] : 1.0f;
   return t;
 }
 
@@ -218,38 +222,65 @@ __device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int
 // (u < VI).  The tile loop hands this to the compute of the current tile,
 // which issues the pieces between its matrix-core segments: issued in one
 // burst, the copies of all waves on a CU queue behind each other in the
-// vector-memory path and stall the waves' in-order issue.
+// vector-memory path and stall the waves' in-order issue.  Every piece is
+// branch-free (wave is wave-uniform, slots past the tile go to the sink), so
+// the pieces do not split the compute into separately scheduled blocks.
 template <int D, bool VI8>
 struct TileCopy {
+  static constexpr int KI = DmaPlan<D>::KI;
+  static constexpr int VI = VI8 ? 0 : DmaPlan<D>::VI;
+  static constexpr int PIECES = KI + VI;   // direct loads per wave for one K tile and one V tile
   __amdgpu_buffer_rsrc_t krs, vrs;   // K (int8) and bf16 V of this head
-  uint32_t koff, voff;               // byte offsets of the tile's first K / V row
-  uint32_t lds;                      // destination stage (LDS byte address)
+  uint32_t koff, voff;               // byte offsets of the K tile's / V tile's first row
+  uint32_t klds, vlds;               // destination K and V stages (LDS byte addresses)
+  uint32_t sink;                     // 1 KiB of LDS that nothing reads
   const DmaPlan<D>* plan;
-  int wave;
-  bool active;                       // false: nothing to copy
+  int wave;                          // wave-uniform, 0..3
   __device__ __forceinline__ void k(int u) const {
     const int inst = wave + 4 * u;
-    if (active && u < DmaPlan<D>::KI && inst < FwdLds<D>::KU) lds_dma16(krs, plan->koff[u], koff, lds + inst * 1024);
+    lds_dma16(krs, plan->koff[u], koff, inst < FwdLds<D>::KU ? klds + inst * 1024 : sink);
   }
   __device__ __forceinline__ void v(int u) const {
     const int inst = wave + 4 * u;
-    if (!VI8 && active && u < DmaPlan<D>::VI && inst < FwdLds<D>::VU)
-      lds_dma16(vrs, plan->voff[u], voff, lds + FwdLds<D>::V_OFF + inst * 1024);
+    lds_dma16(vrs, plan->voff[u], voff, inst < FwdLds<D>::VU ? vlds + inst * 1024 : sink);
+  }
+  // piece p < KI: K load p; otherwise V load p - KI
+  __device__ __forceinline__ void piece(int p) const {
+    if (p < KI) k(p);
+    else if (p < PIECES) v(p - KI);
+  }
+  __device__ __forceinline__ void all_k() const {
+#pragma unroll
+    for (int u = 0; u < KI; ++u) k(u);
   }
   __device__ __forceinline__ void all() const {
 #pragma unroll
-    for (int u = 0; u < DmaPlan<D>::KI; ++u) k(u);
-#pragma unroll
-    for (int u = 0; u < DmaPlan<D>::VI; ++u) v(u);
+    for (int p = 0; p < PIECES; ++p) piece(p);
   }
 };
 
+// Copy of the K tile of tk and the V tile of tv (bf16 V only) into the given
+// stages.
 template <int D, bool VI8>
-__device__ __forceinline__ TileCopy<D, VI8> tile_copy(const TileInfo& t, uint8_t* buf, __amdgpu_buffer_rsrc_t krs,
-                                                      __amdgpu_buffer_rsrc_t vrs, const DmaPlan<D>& plan, int wave,
-                                                      bool active) {
-  return TileCopy<D, VI8>{krs, vrs, (uint32_t)(t.krow0 * D), (uint32_t)(t.vrow0 * D * 2), lds_address(buf), &plan,
-                          wave, active};
+__device__ __forceinline__ TileCopy<D, VI8> tile_copy(const TileInfo& tk, const TileInfo& tv, uint8_t* kbuf,
+                                                      uint8_t* vbuf, uint8_t* sink, __amdgpu_buffer_rsrc_t krs,
+                                                      __amdgpu_buffer_rsrc_t vrs, const DmaPlan<D>& plan, int wave) {
+  return TileCopy<D, VI8>{krs,
+                          vrs,
+                          (uint32_t)(tk.krow0 * D),
+                          (uint32_t)(tv.vrow0() * D * 2),
+                          lds_address(kbuf),
+                          lds_address(vbuf),
+                          lds_address(sink),
+                          &plan,
+                          wave};
+}
+
+// Wait for this wave's direct copies, then for the whole workgroup: after it,
+// every copy issued before it by any wave has landed in LDS.
+__device__ __forceinline__ void copies_done_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 // Scores leave the integer MFMA already in float form: the accumulators start
@@ -378,88 +409,110 @@ __device__ __forceinline__ void half_pv(const uint8_t* vbuf, int key0, const uin
                                                         0, 0, 0);
 }
 
-// One exact 64-key tile from a staged buffer, as two 32-key halves.
-//   S^T = K.Q^T on v_mfma_i32_32x32x32_i8 (exact int32); in half h the lane
-//   holds query row n and keys 32h + (i/4)*8 + hh*4 + i%4.
+// The exact 64-key tiles, as a software pipeline over 32-key halves.
+//   S^T = K.Q^T on v_mfma_i32_32x32x32_i8 (exact int32); in a half the lane
+//   holds query row n and keys (i/4)*8 + hh*4 + i%4 of it.
 //   c = a_i * b_j * sm_scale * log2(e); weights p = exp2(S*c - m_run).
-//   The halves are separate online-softmax steps.  Each one first computes
-//   its weights against m_run as it stands and keeps them when every lane's
-//   partial row sum is finite and at most kFastSum; otherwise (the first step,
-//   a jump in the scores) the exact step recomputes them after moving m_run.
-//   A wave issues in order, so the weight work is interleaved by hand with
-//   independent matrix-core work: the weights of half 0 with the QK MFMAs of
-//   half 1, the weights of half 1 with the PV MFMAs of half 0 (one MFMA, then
-//   one or two weight pairs, in fixed scheduling segments).
+//   Each half is its own online-softmax step.  It first computes its weights
+//   against m_run as it stands and keeps them when every lane's partial row
+//   sum is finite and at most kFastSum; otherwise (the first step, a jump in
+//   the scores) the exact step recomputes them after moving m_run.
 //   The row sum adds the bf16-rounded p (v_dot2 with (1,1)), i.e. exactly the
 //   weights the PV product uses.
 //   O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16.
-// MASKED is the tile holding the end of the valid keys (keys >= nvalid drop).
-template <int D, bool VI8, bool MASKED>
-__device__ __forceinline__ void exact_tile(const uint8_t* buf, const v4i (&qreg)[D / 32], const v16i& magic,
-                                           v16f (&O)[D / 32], float& m_run, float& l_run, float c, float pscale,
-                                           int nvalid, int klane, int vlane, int hh, const TileCopy<D, VI8>& cp) {
+// A wave issues in order and its weights are VALU work that can only overlap
+// matrix-core work it issues in between, so step h of the pipeline puts the
+// QK^T product of half h+1 and the PV product of half h-1 (12 MFMAs for
+// d = 128) on the matrix cores and computes the 8 weight pairs of half h in
+// their shadow, one MFMA and at most one pair per fixed scheduling segment.
+
+template <bool B>
+struct Parity {
+  static constexpr bool value = B;
+};
+
+// MFMA m of a step with NQ QK MFMAs and NP PV MFMAs: QK and PV alternate
+// while both are left (QK first, so the next scores are ready early).
+template <int NQ, int NP>
+__device__ constexpr bool step_is_qk(int m) {
+  return NP == 0 || (NQ > 0 && m < 2 * NQ && m % 2 == 0);
+}
+template <int NQ, int NP>
+__device__ constexpr int step_index(int m) {
+  return (NQ == 0 || NP == 0) ? m : (m < 2 * NQ ? m / 2 : m - NQ);
+}
+
+// One pipeline step.  kh: the K half whose scores go to s_next (DO_QK);
+// vh: the V half (32 rows) that p_prev weighs (DO_PV); s_cur: the scores
+// whose weights go to p_cur (DO_W), with their row-sum part added to l_run
+// after the fast-path check.  The copy pieces [P0, P1) of cp are issued in
+// between.
+template <int D, bool VI8, bool DO_QK, bool DO_PV, bool DO_W, int P0, int P1>
+__device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, const v4i (&qreg)[D / 32],
+                                          const v16i& magic, v16i& s_next, const v16i& s_cur,
+                                          const uint32_t (&p_prev)[8], uint32_t (&p_cur)[8], v16f (&O)[D / 32],
+                                          float& m_run, float& l_run, float c, float pscale, int klane, int vlane,
+                                          int hh, const TileCopy<D, VI8>& cp) {
+  constexpr int NS = D / 32;
+  constexpr int NQ = DO_QK ? NS : 0, NP = DO_PV ? 2 * NS : 0, M = NQ + NP, NC = P1 - P0;
+  static_assert(M > 0, "a step issues matrix work");
+  // A operands, loaded two MFMAs ahead (K rows: 16 int8 channels; V^T: 8 bf16)
+  v4i op[M];
+  auto load = [&](int m) {
+    const int x = step_index<NQ, NP>(m);
+    if (step_is_qk<NQ, NP>(m)) op[m] = *reinterpret_cast<const v4i*>(kh + klane + x * 32);
+    else op[m] = __builtin_bit_cast(v4i, v_frag<D>(vh, 0, x, vlane));
+  };
+  float ps = 0.0f;
+  const float b = -__builtin_fmaf(kMagicF, c, m_run);
+  load(0);
+  if (M > 1) load(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int x = step_index<NQ, NP>(m);
+    if (step_is_qk<NQ, NP>(m))
+      s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(op[m], qreg[x], x == 0 ? magic : s_next, 0, 0, 0);
+    else
+      O[x % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, op[m]), p_frag<D>(p_prev, x),
+                                                          O[x % NS], 0, 0, 0);
+    if (m + 2 < M) load(m + 2);
+    if (DO_W) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e * M / 8 == m) weight_pair<VI8>(s_cur, e, c, b, pscale, ps, p_cur);
+    }
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      if ((2 * k + 1) * M / (2 * (NC > 0 ? NC : 1)) == m) cp.piece(P0 + k);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (DO_W) {
+    if (!fast_ok(ps)) ps = half_exact<NS, VI8, false>(s_cur, 0, c, pscale, kTile, hh, O, m_run, l_run, p_cur);
+    l_run += ps;
+  }
+}
+
+// The tile holding the end of a segment's valid keys (keys >= nvalid drop),
+// done on its own with the exact step for both halves.
+template <int D, bool VI8>
+__device__ __forceinline__ void masked_tile(const uint8_t* kbuf, const uint8_t* vbuf, const v4i (&qreg)[D / 32],
+                                            const v16i& magic, v16f (&O)[D / 32], float& m_run, float& l_run,
+                                            float c, float pscale, int nvalid, int klane, int vlane, int hh) {
   using L = FwdLds<D>;
   constexpr int NS = D / 32;
-  const uint8_t* vbuf = buf + L::V_OFF;
-  v4i k0[NS], k1[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    k0[s] = *reinterpret_cast<const v4i*>(buf + klane + s * 32);
-    k1[s] = *reinterpret_cast<const v4i*>(buf + klane + 32 * L::KSTR + s * 32);
-  }
   v16i acc0 = magic, acc1 = magic;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0[s], qreg[s], acc0, 0, 0, 0);
+  for (int s = 0; s < NS; ++s) {
+    acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(kbuf + klane + s * 32), qreg[s], acc0,
+                                                 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+        *reinterpret_cast<const v4i*>(kbuf + klane + 32 * L::KSTR + s * 32), qreg[s], acc1, 0, 0, 0);
+  }
   uint32_t pw0[8], pw1[8];
-  if (MASKED) {
-    cp.all();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[s], qreg[s], acc1, 0, 0, 0);
-    l_run += half_exact<NS, VI8, true>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
-    half_pv<D>(vbuf, 0, pw0, O, vlane);
-    l_run += half_exact<NS, VI8, true>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
-    half_pv<D>(vbuf, 32, pw1, O, vlane);
-    return;
-  }
-  // QK of half 1, interleaved with the weights of half 0 (8 pairs).
-  float ps0 = 0.0f;
-  {
-    const float b = -__builtin_fmaf(kMagicF, c, m_run);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1[s], qreg[s], acc1, 0, 0, 0);
-      cp.k(s);                                            // next tile's K copies
-#pragma unroll
-      for (int e = s * (8 / NS); e < (s + 1) * (8 / NS); ++e) weight_pair<VI8>(acc0, e, c, b, pscale, ps0, pw0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int u = NS; u < DmaPlan<D>::KI; ++u) cp.k(u);
-  }
-  if (!fast_ok(ps0)) ps0 = half_exact<NS, VI8, false>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
-  l_run += ps0;
-  // PV of half 0 (2*NS MFMAs), interleaved with the weights of half 1.
-  float ps1 = 0.0f;
-  {
-    const float b = -__builtin_fmaf(kMagicF, c, m_run);
-    v8bf vf = v_frag<D>(vbuf, 0, 0, vlane);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 2 * NS; ++i) {
-      const v8bf vn = v_frag<D>(vbuf, 0, i + 1 < 2 * NS ? i + 1 : i, vlane);
-      O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_frag<D>(pw0, i), O[i % NS], 0, 0, 0);
-      cp.v(i);                                            // next tile's V copies
-#pragma unroll
-      for (int e = i * 8 / (2 * NS); e < (i + 1) * 8 / (2 * NS); ++e) weight_pair<VI8>(acc1, e, c, b, pscale, ps1, pw1);
-      vf = vn;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int u = 2 * NS; u < DmaPlan<D>::VI; ++u) cp.v(u);
-  }
-  if (!fast_ok(ps1)) ps1 = half_exact<NS, VI8, false>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
-  l_run += ps1;
+  l_run += half_exact<NS, VI8, true>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
+  half_pv<D>(vbuf, 0, pw0, O, vlane);
+  l_run += half_exact<NS, VI8, true>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
   half_pv<D>(vbuf, 32, pw1, O, vlane);
 }
 
@@ -470,16 +523,20 @@ template <int D, bool VI8, bool OBF16>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using L = FwdLds<D>;
   constexpr int NS = D / 32;   // int8 k-steps of 32 channels; also 32-channel output blocks
-  // Two pipeline stages as separate LDS objects, so the compiler can see that
-  // reading one stage does not depend on the direct loads into the other.
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[L::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[L::STAGE];
+  // Two K and two V stages as separate LDS objects, so the compiler can see
+  // that reading one stage does not depend on the direct loads into another.
+  __shared__ __attribute__((aligned(16))) uint8_t kst0[L::KST];
+  __shared__ __attribute__((aligned(16))) uint8_t kst1[L::KST];
+  __shared__ __attribute__((aligned(16))) uint8_t vst0[L::VST];
+  __shared__ __attribute__((aligned(16))) uint8_t vst1[L::VST];
+  __shared__ __attribute__((aligned(16))) uint8_t sink[1024];   // copy slots past a tile's end
   __shared__ uint16_t elist[2 * kWin];
   __shared__ uint16_t clist[kWin];
   __shared__ int plist[kMaxSegments], pvalid[kMaxSegments];
   __shared__ float bias[32];
   __shared__ int cnts[3];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  __builtin_assume(wave >= 0 && wave < 4);
   const int n = lane & 31, hh = lane >> 5;
   // per-lane LDS byte offsets within a stage: K fragment (row n, channels
   // hh*16..) and V^T fragment (see v_frag)
@@ -571,46 +628,80 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     __syncthreads();
     const int nE = cnts[0], nC = cnts[1], nP = cnts[2];
 
-    // ---------------- exact 64-key tiles, two-stage pipeline ----------------
+    // ---------------- exact 64-key tiles, software pipeline ----------------
+    // Tile T's halves are pipeline steps 2T and 2T+1 (see pipe_step).  K
+    // stages hold tiles by parity and V stages too, one tile behind: between
+    // the barriers that open tile iterations T and T+1 the waves read K of
+    // tile T+1 and V of tile T while the copies of K of tile T+2 and V of tile
+    // T+1 fill the other two stages.  When no tile T+2 exists the K copy
+    // repeats tile T+1 into the free stage, which nothing reads.
+    // Registers: scores of even halves sA, odd halves sB; weights pA / pB.
     if (nE > 0) {
-      TileInfo cur = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS), nxt = cur;
-      if (VI8) load_v_int8<D>(v8base + (int64_t)cur.vrow0 * D, vr, tid);
-      tile_copy<D, VI8>(cur, stage0, krs, vrs, plan, wave, true).all();
-      if (VI8) store_v_int8<D>(stage0, vr, tid);
-      for (int e = 0; e < nE; e += 2) {
-        __syncthreads();                         // tile e is in stage0; stage1 is free
-        const bool more1 = e + 1 < nE;
-        if (more1) {
-          nxt = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 1]), nKS, nVS);
-          if (VI8) load_v_int8<D>(v8base + (int64_t)nxt.vrow0 * D, vr, tid);
-        }
-        exact_tile<D, VI8, false>(stage0, qreg, magic, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, klane, vlane, hh,
-                                  tile_copy<D, VI8>(nxt, stage1, krs, vrs, plan, wave, more1));
-        if (!more1) break;
-        if (VI8) store_v_int8<D>(stage1, vr, tid);
-        cur = nxt;
-        __syncthreads();                         // tile e+1 is in stage1; stage0 is free
-        const bool more2 = e + 2 < nE;
-        if (more2) {
-          nxt = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[e + 2]), nKS, nVS);
-          if (VI8) load_v_int8<D>(v8base + (int64_t)nxt.vrow0 * D, vr, tid);
-        }
-        exact_tile<D, VI8, false>(stage1, qreg, magic, O, m_run, l_run, qc * cur.kscale, cur.pscale, kTile, klane, vlane, hh,
-                                  tile_copy<D, VI8>(nxt, stage0, krs, vrs, plan, wave, more2));
-        if (VI8 && more2) store_v_int8<D>(stage0, vr, tid);
-        cur = nxt;
+      constexpr int PH = (TileCopy<D, VI8>::PIECES + 1) / 2;   // copy pieces in a tile's first step
+      constexpr int PN = TileCopy<D, VI8>::PIECES;
+      TileInfo t0 = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS);
+      TileInfo t1 = nE > 1 ? fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[1]), nKS, nVS) : t0;
+      if (VI8) load_v_int8<D>(v8base + (int64_t)t0.vrow0() * D, vr, tid);
+      tile_copy<D, VI8>(t0, t0, kst0, vst0, sink, krs, vrs, plan, wave).all();
+      tile_copy<D, VI8>(t1, t1, kst1, vst1, sink, krs, vrs, plan, wave).all_k();
+      if (VI8) store_v_int8<D>(vst0, vr, tid);
+      copies_done_barrier();
+      v16i sA, sB;
+      uint32_t pA[8], pB[8];
+      // step 0: scores of half 0 first, then half 1's with half 0's weights
+      pipe_step<D, VI8, true, false, false, 0, 0>(kst0, vst0, qreg, magic, sA, sB, pB, pA, O, m_run, l_run, 0.0f, 0.0f,
+                                                  klane, vlane, hh, TileCopy<D, VI8>{});
+      pipe_step<D, VI8, true, false, true, 0, 0>(kst0 + 32 * L::KSTR, vst0, qreg, magic, sB, sA, pB, pA, O, m_run,
+                                                 l_run, qc * t0.kscale, t0.pscale, klane, vlane, hh,
+                                                 TileCopy<D, VI8>{});
+      // Tile iteration T (T + 1 < nE), between the barrier that opens it and
+      // the next one: steps 2T+1 and 2T+2.  ODD is T's parity, which picks the
+      // stages at compile time.
+      auto tile_iter = [&](auto odd, int T) {
+        constexpr bool ODD = decltype(odd)::value;
+        uint8_t* const krd = ODD ? kst0 : kst1;   // K of tile T+1
+        uint8_t* const vrd = ODD ? vst1 : vst0;   // V of tile T
+        uint8_t* const kwr = ODD ? kst1 : kst0;   // K of tile T+2 goes here
+        uint8_t* const vwr = ODD ? vst0 : vst1;   // V of tile T+1 goes here
+        copies_done_barrier();
+        const TileInfo t2 =
+            T + 2 < nE ? fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[T + 2]), nKS, nVS)
+                       : t1;
+        if (VI8) load_v_int8<D>(v8base + (int64_t)t1.vrow0() * D, vr, tid);
+        const TileCopy<D, VI8> cp = tile_copy<D, VI8>(t2, t1, kwr, vwr, sink, krs, vrs, plan, wave);
+        pipe_step<D, VI8, true, true, true, 0, PH>(krd, vrd, qreg, magic, sA, sB, pA, pB, O, m_run, l_run,
+                                                   qc * t0.kscale, t0.pscale, klane, vlane, hh, cp);
+        pipe_step<D, VI8, true, true, true, PH, PN>(krd + 32 * L::KSTR, vrd + 32 * L::VSTR, qreg, magic, sB, sA, pB,
+                                                    pA, O, m_run, l_run, qc * t1.kscale, t1.pscale, klane, vlane, hh,
+                                                    cp);
+        if (VI8) store_v_int8<D>(vwr, vr, tid);
+        t0 = t1;
+        t1 = t2;
+      };
+      int T = 0;
+      for (; T + 2 < nE; T += 2) {
+        tile_iter(Parity<false>{}, T);
+        tile_iter(Parity<true>{}, T + 1);
       }
+      if (T + 1 < nE) tile_iter(Parity<false>{}, T++);
+      // last tile T: PV of its first half with the weights of its second, then
+      // PV of the second (no copies are in flight, so the stage can be picked
+      // at run time)
+      copies_done_barrier();
+      const uint8_t* vl = (T & 1) ? vst1 : vst0;
+      pipe_step<D, VI8, false, true, true, 0, 0>(kst0, vl, qreg, magic, sA, sB, pA, pB, O, m_run, l_run,
+                                                 qc * t0.kscale, t0.pscale, klane, vlane, hh, TileCopy<D, VI8>{});
+      half_pv<D>(vl, 32, pB, O, vlane);
     }
-    __syncthreads();                             // stages free again
+    copies_done_barrier();                       // stages free again
     for (int pi = 0; pi < nP; ++pi) {            // tiles with the end of a segment's valid keys
       const TileInfo t = fetch_tile<VI8>(a, bh, plist[pi], nKS, nVS);
       const int nvalid = pvalid[pi];
-      if (VI8) load_v_int8<D>(v8base + (int64_t)t.vrow0 * D, vr, tid);
-      tile_copy<D, VI8>(t, stage0, krs, vrs, plan, wave, true).all();
-      if (VI8) store_v_int8<D>(stage0, vr, tid);
-      __syncthreads();
-      exact_tile<D, VI8, true>(stage0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, nvalid,
-                               klane, vlane, hh, tile_copy<D, VI8>(t, stage1, krs, vrs, plan, wave, false));
+      if (VI8) load_v_int8<D>(v8base + (int64_t)t.vrow0() * D, vr, tid);
+      tile_copy<D, VI8>(t, t, kst0, vst0, sink, krs, vrs, plan, wave).all();
+      if (VI8) store_v_int8<D>(vst0, vr, tid);
+      copies_done_barrier();
+      masked_tile<D, VI8>(kst0, vst0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, nvalid, klane, vlane, hh);
       __syncthreads();
     }
 
@@ -640,10 +731,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           vhi[e2] = (__bf16)vf[e2];
           vlo[e2] = (__bf16)(vf[e2] - (float)vhi[e2]);
         }
-        *reinterpret_cast<v4bf*>(stage0 + col * L::KCSTR + c4 * 8) = khi;
-        *reinterpret_cast<v4bf*>(stage0 + L::KCL_OFF + col * L::KCSTR + c4 * 8) = klo;
-        *reinterpret_cast<v4bf*>(stage1 + col * L::VSTR + c4 * 8) = vhi;
-        *reinterpret_cast<v4bf*>(stage1 + L::VCL_OFF + col * L::VSTR + c4 * 8) = vlo;
+        *reinterpret_cast<v4bf*>(vst0 + col * L::KCSTR + c4 * 8) = khi;
+        *reinterpret_cast<v4bf*>(vst0 + L::KCL_OFF + col * L::KCSTR + c4 * 8) = klo;
+        *reinterpret_cast<v4bf*>(vst1 + col * L::VSTR + c4 * 8) = vhi;
+        *reinterpret_cast<v4bf*>(vst1 + L::VCL_OFF + col * L::VSTR + c4 * 8) = vlo;
         if (c4 == 0) bias[col] = cn > 0.0f ? __log2f(cn) : -INFINITY;
       }
       __syncthreads();
@@ -654,8 +745,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int pp = 0; pp < 2; ++pp) {
           const v8bf qb = i8x8_to_bf16(qreg[s][2 * pp], qreg[s][2 * pp + 1]);
           const int off = n * L::KCSTR + (s * 32 + hh * 16 + pp * 8) * 2;
-          const v8bf khi = *reinterpret_cast<const v8bf*>(stage0 + off);
-          const v8bf klo = *reinterpret_cast<const v8bf*>(stage0 + L::KCL_OFF + off);
+          const v8bf khi = *reinterpret_cast<const v8bf*>(vst0 + off);
+          const v8bf klo = *reinterpret_cast<const v8bf*>(vst0 + L::KCL_OFF + off);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb, acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qb, acc, 0, 0, 0);
         }
@@ -688,8 +779,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NS; ++cb) {
           const int col = cb * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
-          const uint8_t* ph = stage1 + krow * L::VSTR + col * 2;
-          const uint8_t* pl = stage1 + L::VCL_OFF + krow * L::VSTR + col * 2;
+          const uint8_t* ph = vst1 + krow * L::VSTR + col * 2;
+          const uint8_t* pl = vst1 + L::VCL_OFF + krow * L::VSTR + col * 2;
           const v8bf vh = cat8(tr16(ph), tr16(ph + 8 * L::VSTR));
           const v8bf vl = cat8(tr16(pl), tr16(pl + 8 * L::VSTR));
           O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pf, O[cb], 0, 0, 0);
