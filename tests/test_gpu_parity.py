@@ -303,6 +303,31 @@ def test_float_qk_forward(sa, orc, d, G, kblock, valid):
     _check_workload(orc, wl, tau=0.5)
 
 
+@pytest.mark.parametrize("kblock,G,v_int8,d", [(64, 1, False, 128), (64, 0, False, 64), (128, 0, True, 128),
+                                                (128, 2, False, 64)])
+def test_exact_tile_counts(sa, orc, kblock, G, v_int8, d):
+    """Explicit maps giving the query blocks 0..7 exact key blocks each (the
+    rest centroids, or dropped without centroids): the forward's tile loop
+    runs every small count of exact tiles, ends on both tile parities, and
+    meets the tile holding the end of the valid keys (1000 of 1024)."""
+    L, H = 1024, 2
+    wl = W.tiny_sol(seed=61, H=H, L=L, d=d, valid=1000, centroids_per_block=G)
+    wl.kblock = wl.k_scale_rows = wl.map_kblock = kblock
+    if v_int8:
+        wl.v_int8, wl.v_scale_rows = True, kblock
+    nQB, nKB = L // 128, L // kblock
+    rng = np.random.default_rng(62)
+    em = np.full((1, H, nQB, nKB), CENTROID if G > 0 else DROP, np.uint8)
+    for h in range(H):
+        for i in range(nQB):
+            n = (i + 3 * h) % 8
+            em[0, h, i, rng.choice(nKB, size=n, replace=False)] = EXACT
+    wl.explicit_map = em
+    g, o = _check_workload(orc, wl)
+    counts = (g["map"] == EXACT).sum(-1)
+    assert set(counts.ravel().tolist()) == set(range(8))
+
+
 def test_float_qk_prefix_and_segments(sa, orc):
     wl = W.config(4, small=True)
     wl.qk_float = True
