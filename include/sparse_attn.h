@@ -3,10 +3,10 @@
  * library (libsparse_attn.so).
  *
  * The method (Configure Sol Sparse Attention, "How it works"): Q and K are
- * quantized to INT8 per block; for every 128-token query block each 64-token
- * key/value block gets a cheap proxy score on those INT8 tensors; a block whose
+ * quantized to INT8 per block; within each 128-token query block every 64-token
+ * key/value block is rated by an inexpensive proxy on those INT8 tensors; a block whose
  * score exceeds mean + routing_threshold * std over the query block's candidates
- * is skipped and replaced by one 64-token centroid (1x64) or two 32-token
+ * is skipped, standing in as a single 64-token centroid (1x64) or two 32-token
  * centroids (2x32) that still enter the online softmax; the other blocks are
  * computed exactly (INT8 QK^T, fp32 online softmax, bf16 PV).  A leading prefix
  * of conditioning tokens can be exempted (Configure Sol Sparse Attention, "The
@@ -160,8 +160,8 @@ int32_t quantize_qk_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL,
                          int32_t rows_per_block, int8_t* x_q, float* scale, void* stream);
 
 /* Streaming INT8 K/V cache append (FlashVSR Kitchen Sparse Attention, opening
- * section: the streaming modes keep a sliding cache of past K/V in every
- * block, stored as INT8 in bounded 128-row slabs).  The cache of one tensor (K
+ * section: in streaming use each block holds the recent K/V history as INT8,
+ * bounded, in 128-row slabs).  The cache of one tensor (K
  * or V) is a ring of `slots` slabs of rows_per_slab rows per (b, h).  The new
  * chunk is quantized per slab exactly as quantize_qk_int8 quantizes blocks, and
  * slab s of it replaces ring slot (first_slot + s) mod slots, evicting the slab

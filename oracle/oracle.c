@@ -8,9 +8,9 @@
  *
  * What it computes follows the pages' statement of the method:
  *   - Configure Sol Sparse Attention, "How it works": per 128-token query block,
- *     every 64-token K/V block gets a cheap proxy score computed on the same
- *     prequantized INT8 Q/K as the exact path; a block is skipped when its score
- *     exceeds mean + routing_threshold * std; skipped blocks become one 64-token
+ *     each 64-token K/V block is rated by an inexpensive proxy taken from the
+ *     INT8 Q/K that the exact tiles also use; blocks rated above
+ *     mean + routing_threshold * std are not computed exactly but become one 64-token
  *     centroid (1x64) or two 32-token centroids (2x32) that still enter the
  *     online softmax.
  *   - Configure Sol Sparse Attention, "The inputs that matter": routing_threshold
@@ -130,8 +130,8 @@ static double v_at(const orc_vsrc* s, int b, int h, int r, int c) {
 
 /* ------------------------------------------------------------------------- */
 /* Streaming INT8 K/V cache (FlashVSR Kitchen Sparse Attention, opening      */
-/* section: the streaming modes keep a sliding cache of past K/V in every   */
-/* block, stored as INT8 in bounded 128-row slabs).  The cache is a ring of  */
+/* section: in streaming use each block holds the recent K/V history as    */
+/* INT8, bounded, in 128-row slabs).  The cache is a ring of                 */
 /* `slots` slabs of R rows per (b, h).  A chunk of `rows` new rows is        */
 /* quantized per slab of R rows exactly as orc_quantize does (rows at or     */
 /* past valid_len are padding), and slab s of the chunk replaces ring slot   */

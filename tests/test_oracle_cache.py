@@ -1,8 +1,8 @@
 """Pins for the oracle's streaming INT8 K/V cache (CPU only).
 
-FlashVSR Kitchen Sparse Attention, opening section: streaming modes keep a
-sliding cache of past K/V tensors in every block, as INT8 in bounded 128-row
-slabs.  The cache is a ring of slabs; each new slab evicts the oldest.
+FlashVSR Kitchen Sparse Attention, opening section: in streaming use each
+block holds the recent K/V history as INT8, bounded, in 128-row slabs.  The
+cache is a ring of slabs; each new slab evicts the oldest.
 """
 import numpy as np
 import pytest

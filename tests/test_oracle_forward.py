@@ -1,7 +1,7 @@
 """Pins for the oracle's forward pass (CPU only).
 
 Configure Sol Sparse Attention, "How it works": kept blocks are computed exactly
-on the INT8 Q/K; skipped blocks are replaced by one 64-token centroid (1x64) or
+on the INT8 Q/K; a skipped block stands in as a single 64-token centroid (1x64) or
 two 32-token centroids (2x32) that still contribute to the softmax.  Configure H3
 Static Virtual KV, mode list ("residual"): centroids share the online softmax
 with the exact blocks.  FlashVSR Sparge Attention, opening section: a dense

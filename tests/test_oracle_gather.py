@@ -1,9 +1,9 @@
 """Pins for the oracle's virtual-KV gather (CPU only).
 
 Configure H3 Static Virtual KV, mode list: "conservative" materializes the exact
-seven-slice K/V; "fast" re-reads each logical slice from one of the two physical
-bf16 slices through a source map, applies that slice's temporal rotary phase,
-and only materializes INT8 — with nothing approximated.
+seven-slice K/V; "fast" builds each logical slice by reading a physical bf16
+slice (one of two) named by a source map, applies that slice's temporal rotary
+phase, and only materializes INT8 — with nothing approximated.
 """
 import numpy as np
 
