@@ -706,36 +706,53 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
 
     // ---------------- centroid columns, 32 at a time ----------------
+    // Staging: 8 threads per column, each converting CE consecutive 4-channel
+    // pieces of one centroid to bf16 hi+lo pairs.  Column (key block j, group
+    // g) is row j*G + g of this head's centroids (G is 1 or 2 here).  The rows
+    // are loaded whatever the count; a count of 0 only selects zeros.
     const int ncols = nC * a.G;
+    constexpr int CE = D / 32;
+    const int64_t chead = bh * a.nKB * a.G;
+    const float* kch = a.kc + chead * D;
+    const float* vch = a.vc + chead * D;
+    const float* cnh = a.cnt + chead;
     for (int c0 = 0; c0 < ncols; c0 += 32) {
-      for (int idx = tid; idx < 32 * (D / 4); idx += 256) {
-        const int col = idx / (D / 4), c4 = idx % (D / 4);
-        const int ent = c0 + col, be = ent / a.G, g = ent % a.G;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      {
+        const int col = tid >> 3, q = tid & 7;
+        const int ent = c0 + col, be = a.G == 2 ? ent >> 1 : ent, g = a.G == 2 ? ent & 1 : 0;
         float cn = 0.0f;
+        float4 kv[CE], vv[CE];
+#pragma unroll
+        for (int e = 0; e < CE; ++e) kv[e] = vv[e] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (be < nC) {
-          const int j = w0 + clist[be];
-          const int64_t ci = (bh * a.nKB + j) * a.G + g;
-          cn = a.cnt[ci];
-          if (cn > 0.0f) {
-            kv = *reinterpret_cast<const float4*>(a.kc + ci * D + c4 * 4);
-            vv = *reinterpret_cast<const float4*>(a.vc + ci * D + c4 * 4);
+          const int cl = (w0 + clist[be]) * a.G + g;
+          cn = cnh[cl];
+#pragma unroll
+          for (int e = 0; e < CE; ++e) {
+            kv[e] = reinterpret_cast<const float4*>(kch + cl * D)[q * CE + e];
+            vv[e] = reinterpret_cast<const float4*>(vch + cl * D)[q * CE + e];
           }
         }
-        const float kf[4] = {kv.x, kv.y, kv.z, kv.w}, vf[4] = {vv.x, vv.y, vv.z, vv.w};
-        v4bf khi, klo, vhi, vlo;
+        const bool has = cn > 0.0f;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          khi[e2] = (__bf16)kf[e2];
-          klo[e2] = (__bf16)(kf[e2] - (float)khi[e2]);
-          vhi[e2] = (__bf16)vf[e2];
-          vlo[e2] = (__bf16)(vf[e2] - (float)vhi[e2]);
+        for (int e = 0; e < CE; ++e) {
+          const int c4 = q * CE + e;
+          const float kf[4] = {kv[e].x, kv[e].y, kv[e].z, kv[e].w}, vf[4] = {vv[e].x, vv[e].y, vv[e].z, vv[e].w};
+          v4bf khi, klo, vhi, vlo;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float kx = has ? kf[e2] : 0.0f, vx = has ? vf[e2] : 0.0f;
+            khi[e2] = (__bf16)kx;
+            klo[e2] = (__bf16)(kx - (float)khi[e2]);
+            vhi[e2] = (__bf16)vx;
+            vlo[e2] = (__bf16)(vx - (float)vhi[e2]);
+          }
+          *reinterpret_cast<v4bf*>(vst0 + col * L::KCSTR + c4 * 8) = khi;
+          *reinterpret_cast<v4bf*>(vst0 + L::KCL_OFF + col * L::KCSTR + c4 * 8) = klo;
+          *reinterpret_cast<v4bf*>(vst1 + col * L::VSTR + c4 * 8) = vhi;
+          *reinterpret_cast<v4bf*>(vst1 + L::VCL_OFF + col * L::VSTR + c4 * 8) = vlo;
         }
-        *reinterpret_cast<v4bf*>(vst0 + col * L::KCSTR + c4 * 8) = khi;
-        *reinterpret_cast<v4bf*>(vst0 + L::KCL_OFF + col * L::KCSTR + c4 * 8) = klo;
-        *reinterpret_cast<v4bf*>(vst1 + col * L::VSTR + c4 * 8) = vhi;
-        *reinterpret_cast<v4bf*>(vst1 + L::VCL_OFF + col * L::VSTR + c4 * 8) = vlo;
-        if (c4 == 0) bias[col] = cn > 0.0f ? __log2f(cn) : -INFINITY;
+        if (q == 0) bias[col] = has ? __log2f(cn) : -INFINITY;
       }
       __syncthreads();
       v16f acc = (v16f){};
