@@ -37,19 +37,41 @@ namespace {
 constexpr int kWin = 512;      // map entries scanned per list-building window
 constexpr float kLazy = 8.0f;  // rescale O only when the row max grows by more than 2^8
 
+// LDS layout of the K and V tiles and of the centroid staging: unpadded rows
+// with their 16-byte units (K) or 64-byte segments (V) permuted per row by an
+// XOR, so the readers' access patterns hit distinct banks without padding:
+//  * K rows are read with ds_read_b128, 16 lanes per cycle on 16 consecutive
+//    rows at the same logical unit; a 256-byte bank line holds 256/KROW rows,
+//    and rows of one line get their units XORed with different values.
+//  * V rows are read with ds_read_b64_tr_b16, 16 lanes per cycle on 4
+//    consecutive rows x 32 bytes; rows of different lines sharing the bank
+//    positions get their 64-byte segments XORed with different values.
+// Every row's data stays inside its own row, so a whole tile is one
+// contiguous run of 1 KiB copy chunks (no padding lanes).
 template <int D>
 struct FwdLds {
-  static constexpr int KSTR = D + 16;         // int8 K tile row stride (bytes)
-  static constexpr int VSTR = 2 * D + 64;     // bf16 V tile row stride (bytes)
-  static constexpr int KCSTR = 2 * D + 16;    // bf16 centroid-K row stride (bytes)
-  static constexpr int KU = KSTR / 16;        // 16-byte units per K row (last one padding)
-  static constexpr int VU = VSTR / 16;        // 16-byte units per V row (last four padding)
-  static constexpr int KST = kTile * KSTR;    // one K stage
-  static constexpr int VST = kTile * VSTR;    // one V stage
+  static constexpr int KROW = D;              // int8 K tile row (bytes)
+  static constexpr int VROW = 2 * D;          // bf16 V tile row (bytes)
+  static constexpr int KCROW = 2 * D;         // bf16 centroid-K row (bytes)
+  static constexpr int KU = KROW / 16;        // 16-byte units per K row = 1 KiB copies per K tile
+  static constexpr int VU = VROW / 16;        // 16-byte units per V row = 1 KiB copies per V tile
+  static constexpr int KST = kTile * KROW;    // one K stage
+  static constexpr int VST = kTile * VROW;    // one V stage
   // centroid staging: K hi/lo in V stage 0, V hi/lo in V stage 1
-  static constexpr int KCL_OFF = 32 * KCSTR;
-  static constexpr int VCL_OFF = 32 * VSTR;
-  static_assert(2 * 32 * KCSTR <= VST && 2 * 32 * VSTR <= VST, "centroid staging must fit a V stage");
+  static constexpr int KCL_OFF = 32 * KCROW;
+  static constexpr int VCL_OFF = 32 * VROW;
+  static_assert(2 * 32 * KCROW <= VST && 2 * 32 * VROW <= VST, "centroid staging must fit a V stage");
+  static_assert(KU % 4 == 0 && VU % 4 == 0, "tile copies split evenly over 4 waves");
+  // byte offset of (row r, byte x of the row) in a K tile / V tile / centroid-K staging
+  __device__ __forceinline__ static constexpr int k_off(int r, int x) {
+    return r * KROW + (((x >> 4) ^ ((r / (256 / KROW)) & (KU - 1))) << 4) + (x & 15);
+  }
+  __device__ __forceinline__ static constexpr int v_off(int r, int x) {
+    return r * VROW + (((x >> 6) ^ ((r / (VROW >= 256 ? 1 : 256 / VROW)) & (VROW / 64 - 1))) << 6) + (x & 63);
+  }
+  __device__ __forceinline__ static constexpr int kc_off(int r, int x) {
+    return r * KCROW + (((x >> 4) ^ ((r / (KCROW >= 256 ? 1 : 256 / KCROW)) & (KCROW / 16 - 1))) << 4) + (x & 15);
+  }
 };
 
 __device__ __forceinline__ v4bf tr16(const uint8_t* lds_byte_ptr) {
@@ -106,36 +128,33 @@ __device__ __forceinline__ void maybe_rescale(float m_tile, float& m_run, float&
 // Direct copy into LDS of one 64-row K tile (int8) and, unless V arrives as
 // INT8, one 64-row V tile (bf16) with buffer_load_dwordx4 ... lds.  Lane L of
 // a wave instruction lands at LDS offset 16*L of that instruction's 1 KiB
-// chunk, so the padded row layout is produced by picking each lane's source;
-// lanes on padding fetch nothing (kPadOffset).  The per-lane source offsets do
-// not depend on the tile and are computed once; the tile offset is a scalar.
+// chunk, so the permuted row layout is produced by picking each lane's
+// source.  The per-lane source offsets do not depend on the tile and are
+// computed once; the tile offset is a scalar.
 template <int D>
 struct DmaPlan {
-  static constexpr int KI = (FwdLds<D>::KU + 3) / 4;   // K instructions per wave (at most)
-  static constexpr int VI = (FwdLds<D>::VU + 3) / 4;   // V instructions per wave (at most)
+  static constexpr int KI = FwdLds<D>::KU / 4;   // K copies per wave
+  static constexpr int VI = FwdLds<D>::VU / 4;   // V copies per wave
   uint32_t koff[KI];   // unsigned: the copy uses a scalar base plus a 32-bit lane offset
   uint32_t voff[VI];
 };
 
-// Lanes that land on a row's padding get an offset past any buffer's end:
-// the buffer load returns zeros for them without touching memory.
-constexpr uint32_t kPadOffset = 0xFFFFFFF0u;
-
-// Instruction slots past the end of a tile (when its instruction count is not
-// a multiple of 4) fetch nothing on every lane and land in a 1 KiB sink.
+// Lane L of copy chunk c lands at byte 1024c + 16L of the stage; its source is
+// the 16 bytes the layout puts there (XOR is its own inverse, so the logical
+// unit is the stored one XORed with the row's value).
 template <int D>
 __device__ __forceinline__ DmaPlan<D> make_dma_plan(int wave, int lane) {
   using L = FwdLds<D>;
   DmaPlan<D> pl;
 #pragma unroll
   for (int t = 0; t < DmaPlan<D>::KI; ++t) {
-    const int u = (wave + 4 * t) * 64 + lane, row = u / L::KU, c = u % L::KU;
-    pl.koff[t] = row < kTile && c < D / 16 ? (uint32_t)(row * D + c * 16) : kPadOffset;
+    const int pos = (wave + 4 * t) * 1024 + 16 * lane, row = pos / L::KROW;
+    pl.koff[t] = (uint32_t)(row * L::KROW + (L::k_off(row, pos % L::KROW) - row * L::KROW));
   }
 #pragma unroll
   for (int t = 0; t < DmaPlan<D>::VI; ++t) {
-    const int u = (wave + 4 * t) * 64 + lane, row = u / L::VU, c = u % L::VU;
-    pl.voff[t] = row < kTile && c < 2 * D / 16 ? (uint32_t)(row * 2 * D + c * 16) : kPadOffset;
+    const int pos = (wave + 4 * t) * 1024 + 16 * lane, row = pos / L::VROW;
+    pl.voff[t] = (uint32_t)(row * L::VROW + (L::v_off(row, pos % L::VROW) - row * L::VROW));
   }
   return pl;
 }
@@ -162,8 +181,8 @@ __device__ __forceinline__ void store_v_int8(uint8_t* vbuf, const VRegs<D>& vr, 
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) {
     const int v = tid + 256 * e, r = v / (D / 16), cc = v % (D / 16);
-    *reinterpret_cast<v8bf*>(vbuf + r * L::VSTR + cc * 32) = i8x8_to_bf16(vr.r[e][0], vr.r[e][1]);
-    *reinterpret_cast<v8bf*>(vbuf + r * L::VSTR + cc * 32 + 16) = i8x8_to_bf16(vr.r[e][2], vr.r[e][3]);
+    *reinterpret_cast<v8bf*>(vbuf + L::v_off(r, cc * 32)) = i8x8_to_bf16(vr.r[e][0], vr.r[e][1]);
+    *reinterpret_cast<v8bf*>(vbuf + L::v_off(r, cc * 32 + 16)) = i8x8_to_bf16(vr.r[e][2], vr.r[e][3]);
   }
 }
 
@@ -223,8 +242,9 @@ __device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int
 // which issues the pieces between its matrix-core segments: issued in one
 // burst, the copies of all waves on a CU queue behind each other in the
 // vector-memory path and stall the waves' in-order issue.  Every piece is
-// branch-free (wave is wave-uniform, slots past the tile go to the sink), so
-// the pieces do not split the compute into separately scheduled blocks.
+// branch-free (wave is wave-uniform, every wave owns the same number of
+// chunks), so the pieces do not split the compute into separately scheduled
+// blocks.
 template <int D, bool VI8>
 struct TileCopy {
   static constexpr int KI = DmaPlan<D>::KI;
@@ -233,16 +253,13 @@ struct TileCopy {
   __amdgpu_buffer_rsrc_t krs, vrs;   // K (int8) and bf16 V of this head
   uint32_t koff, voff;               // byte offsets of the K tile's / V tile's first row
   uint32_t klds, vlds;               // destination K and V stages (LDS byte addresses)
-  uint32_t sink;                     // 1 KiB of LDS that nothing reads
   const DmaPlan<D>* plan;
   int wave;                          // wave-uniform, 0..3
   __device__ __forceinline__ void k(int u) const {
-    const int inst = wave + 4 * u;
-    lds_dma16(krs, plan->koff[u], koff, inst < FwdLds<D>::KU ? klds + inst * 1024 : sink);
+    lds_dma16(krs, plan->koff[u], koff, klds + (wave + 4 * u) * 1024);
   }
   __device__ __forceinline__ void v(int u) const {
-    const int inst = wave + 4 * u;
-    lds_dma16(vrs, plan->voff[u], voff, inst < FwdLds<D>::VU ? vlds + inst * 1024 : sink);
+    lds_dma16(vrs, plan->voff[u], voff, vlds + (wave + 4 * u) * 1024);
   }
   // piece p < KI: K load p; otherwise V load p - KI
   __device__ __forceinline__ void piece(int p) const {
@@ -263,7 +280,7 @@ struct TileCopy {
 // stages.
 template <int D, bool VI8>
 __device__ __forceinline__ TileCopy<D, VI8> tile_copy(const TileInfo& tk, const TileInfo& tv, uint8_t* kbuf,
-                                                      uint8_t* vbuf, uint8_t* sink, __amdgpu_buffer_rsrc_t krs,
+                                                      uint8_t* vbuf, __amdgpu_buffer_rsrc_t krs,
                                                       __amdgpu_buffer_rsrc_t vrs, const DmaPlan<D>& plan, int wave) {
   return TileCopy<D, VI8>{krs,
                           vrs,
@@ -271,7 +288,6 @@ __device__ __forceinline__ TileCopy<D, VI8> tile_copy(const TileInfo& tk, const 
                           (uint32_t)(tv.vrow0() * D * 2),
                           lds_address(kbuf),
                           lds_address(vbuf),
-                          lds_address(sink),
                           &plan,
                           wave};
 }
@@ -357,10 +373,20 @@ __device__ __forceinline__ float half_exact(const v16i& acc, int key0, float c, 
 // kFastSum.  With m_run = -inf (no step yet) the weights are +inf and fail.
 __device__ __forceinline__ bool fast_ok(float psum) { return __ballot(!(psum <= kFastSum)) == 0; }
 
+// Per-lane LDS offsets of the tile readers (their layout terms depend only on
+// the lane): k[x], the K operand of k-step x (row n, bytes 32x + 16hh);
+// v[c], the V^T operand for output block c (rows hh*4 + j16/4 (+8),
+// bytes 64c + (g16&1)*32 + (j16&3)*8 of the row).
+template <int D>
+struct LaneOffsets {
+  int k[D / 32];
+  int v[D / 32];
+};
+
 // O^T += V^T.P^T for one 32-key half (two k-steps of 16 keys).
 template <int D>
 __device__ __forceinline__ void half_pv(const uint8_t* vbuf, int key0, const uint32_t (&pw)[8], v16f (&O)[D / 32],
-                                        int vlane);
+                                        const LaneOffsets<D>& lo);
 
 // One weight pair (scores 2e, 2e+1 of a half) on the fast path: two FMAs, two
 // exp2, one bf16 pack and the row-sum update.
@@ -382,13 +408,12 @@ __device__ __forceinline__ void weight_pair(const v16i& acc, int e, float c, flo
 }
 
 // V^T operand of PV MFMA i (k-step i / NS of the half, output block i % NS).
-// vlane: the lane's byte offset (hh*4 + j16/4) * VSTR + ((g16&1)*16 + 4*(j16&3)) * 2.
 template <int D>
-__device__ __forceinline__ v8bf v_frag(const uint8_t* vbuf, int key0, int i, int vlane) {
+__device__ __forceinline__ v8bf v_frag(const uint8_t* vbuf, int key0, int i, const LaneOffsets<D>& lo) {
   using L = FwdLds<D>;
   constexpr int NS = D / 32;
-  const uint8_t* p0 = vbuf + vlane + (key0 + (i / NS) * 16) * L::VSTR + (i % NS) * 64;
-  return cat8(tr16(p0), tr16(p0 + 8 * L::VSTR));
+  const uint8_t* p0 = vbuf + lo.v[i % NS] + (key0 + (i / NS) * 16) * L::VROW;
+  return cat8(tr16(p0), tr16(p0 + 8 * L::VROW));
 }
 
 template <int D>
@@ -401,11 +426,11 @@ __device__ __forceinline__ v8bf p_frag(const uint32_t (&pw)[8], int i) {
 
 template <int D>
 __device__ __forceinline__ void half_pv(const uint8_t* vbuf, int key0, const uint32_t (&pw)[8], v16f (&O)[D / 32],
-                                        int vlane) {
+                                        const LaneOffsets<D>& lo) {
   constexpr int NS = D / 32;
 #pragma unroll
   for (int i = 0; i < 2 * NS; ++i)
-    O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(vbuf, key0, i, vlane), p_frag<D>(pw, i), O[i % NS],
+    O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(vbuf, key0, i, lo), p_frag<D>(pw, i), O[i % NS],
                                                         0, 0, 0);
 }
 
@@ -451,8 +476,8 @@ template <int D, bool VI8, bool DO_QK, bool DO_PV, bool DO_W, int P0, int P1>
 __device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, const v4i (&qreg)[D / 32],
                                           const v16i& magic, v16i& s_next, const v16i& s_cur,
                                           const uint32_t (&p_prev)[8], uint32_t (&p_cur)[8], v16f (&O)[D / 32],
-                                          float& m_run, float& l_run, float c, float pscale, int klane, int vlane,
-                                          int hh, const TileCopy<D, VI8>& cp) {
+                                          float& m_run, float& l_run, float c, float pscale,
+                                          const LaneOffsets<D>& lo, int hh, const TileCopy<D, VI8>& cp) {
   constexpr int NS = D / 32;
   constexpr int NQ = DO_QK ? NS : 0, NP = DO_PV ? 2 * NS : 0, M = NQ + NP, NC = P1 - P0;
   static_assert(M > 0, "a step issues matrix work");
@@ -460,8 +485,8 @@ __device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, 
   v4i op[M];
   auto load = [&](int m) {
     const int x = step_index<NQ, NP>(m);
-    if (step_is_qk<NQ, NP>(m)) op[m] = *reinterpret_cast<const v4i*>(kh + klane + x * 32);
-    else op[m] = __builtin_bit_cast(v4i, v_frag<D>(vh, 0, x, vlane));
+    if (step_is_qk<NQ, NP>(m)) op[m] = *reinterpret_cast<const v4i*>(kh + lo.k[x]);
+    else op[m] = __builtin_bit_cast(v4i, v_frag<D>(vh, 0, x, lo));
   };
   float ps = 0.0f;
   const float b = -__builtin_fmaf(kMagicF, c, m_run);
@@ -498,22 +523,21 @@ __device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, 
 template <int D, bool VI8>
 __device__ __forceinline__ void masked_tile(const uint8_t* kbuf, const uint8_t* vbuf, const v4i (&qreg)[D / 32],
                                             const v16i& magic, v16f (&O)[D / 32], float& m_run, float& l_run,
-                                            float c, float pscale, int nvalid, int klane, int vlane, int hh) {
+                                            float c, float pscale, int nvalid, const LaneOffsets<D>& lo, int hh) {
   using L = FwdLds<D>;
   constexpr int NS = D / 32;
   v16i acc0 = magic, acc1 = magic;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(kbuf + klane + s * 32), qreg[s], acc0,
-                                                 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-        *reinterpret_cast<const v4i*>(kbuf + klane + 32 * L::KSTR + s * 32), qreg[s], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(kbuf + lo.k[s]), qreg[s], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(kbuf + 32 * L::KROW + lo.k[s]), qreg[s],
+                                                 acc1, 0, 0, 0);
   }
   uint32_t pw0[8], pw1[8];
   l_run += half_exact<NS, VI8, true>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
-  half_pv<D>(vbuf, 0, pw0, O, vlane);
+  half_pv<D>(vbuf, 0, pw0, O, lo);
   l_run += half_exact<NS, VI8, true>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
-  half_pv<D>(vbuf, 32, pw1, O, vlane);
+  half_pv<D>(vbuf, 32, pw1, O, lo);
 }
 
 
@@ -529,7 +553,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kst1[L::KST];
   __shared__ __attribute__((aligned(16))) uint8_t vst0[L::VST];
   __shared__ __attribute__((aligned(16))) uint8_t vst1[L::VST];
-  __shared__ __attribute__((aligned(16))) uint8_t sink[1024];   // copy slots past a tile's end
   __shared__ uint16_t elist[2 * kWin];
   __shared__ uint16_t clist[kWin];
   __shared__ int plist[kMaxSegments], pvalid[kMaxSegments];
@@ -538,10 +561,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   __builtin_assume(wave >= 0 && wave < 4);
   const int n = lane & 31, hh = lane >> 5;
-  // per-lane LDS byte offsets within a stage: K fragment (row n, channels
-  // hh*16..) and V^T fragment (see v_frag)
-  const int klane = opaque(n * L::KSTR + hh * 16);
-  const int vlane = opaque((hh * 4 + ((lane & 15) >> 2)) * L::VSTR + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2);
+  // per-lane LDS offsets of the tile readers (see LaneOffsets)
+  LaneOffsets<D> lo;
+  {
+    const int vq = hh * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int x = 0; x < NS; ++x) {
+      lo.k[x] = opaque(L::k_off(n, 32 * x + 16 * hh));
+      lo.v[x] = opaque(L::v_off(vq, 64 * x + ((lane >> 4) & 1) * 32 + (lane & 3) * 8));
+    }
+  }
 
   // XCD-aware block order: hardware id b runs on XCD b % 8; give each XCD a
   // contiguous range of (head, query block) work items.
@@ -642,17 +671,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       TileInfo t0 = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS);
       TileInfo t1 = nE > 1 ? fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[1]), nKS, nVS) : t0;
       if (VI8) load_v_int8<D>(v8base + (int64_t)t0.vrow0() * D, vr, tid);
-      tile_copy<D, VI8>(t0, t0, kst0, vst0, sink, krs, vrs, plan, wave).all();
-      tile_copy<D, VI8>(t1, t1, kst1, vst1, sink, krs, vrs, plan, wave).all_k();
+      tile_copy<D, VI8>(t0, t0, kst0, vst0, krs, vrs, plan, wave).all();
+      tile_copy<D, VI8>(t1, t1, kst1, vst1, krs, vrs, plan, wave).all_k();
       if (VI8) store_v_int8<D>(vst0, vr, tid);
       copies_done_barrier();
       v16i sA, sB;
       uint32_t pA[8], pB[8];
       // step 0: scores of half 0 first, then half 1's with half 0's weights
       pipe_step<D, VI8, true, false, false, 0, 0>(kst0, vst0, qreg, magic, sA, sB, pB, pA, O, m_run, l_run, 0.0f, 0.0f,
-                                                  klane, vlane, hh, TileCopy<D, VI8>{});
-      pipe_step<D, VI8, true, false, true, 0, 0>(kst0 + 32 * L::KSTR, vst0, qreg, magic, sB, sA, pB, pA, O, m_run,
-                                                 l_run, qc * t0.kscale, t0.pscale, klane, vlane, hh,
+                                                  lo, hh, TileCopy<D, VI8>{});
+      pipe_step<D, VI8, true, false, true, 0, 0>(kst0 + 32 * L::KROW, vst0, qreg, magic, sB, sA, pB, pA, O, m_run,
+                                                 l_run, qc * t0.kscale, t0.pscale, lo, hh,
                                                  TileCopy<D, VI8>{});
       // Tile iteration T (T + 1 < nE), between the barrier that opens it and
       // the next one: steps 2T+1 and 2T+2.  ODD is T's parity, which picks the
@@ -668,11 +697,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             T + 2 < nE ? fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[T + 2]), nKS, nVS)
                        : t1;
         if (VI8) load_v_int8<D>(v8base + (int64_t)t1.vrow0() * D, vr, tid);
-        const TileCopy<D, VI8> cp = tile_copy<D, VI8>(t2, t1, kwr, vwr, sink, krs, vrs, plan, wave);
+        const TileCopy<D, VI8> cp = tile_copy<D, VI8>(t2, t1, kwr, vwr, krs, vrs, plan, wave);
         pipe_step<D, VI8, true, true, true, 0, PH>(krd, vrd, qreg, magic, sA, sB, pA, pB, O, m_run, l_run,
-                                                   qc * t0.kscale, t0.pscale, klane, vlane, hh, cp);
-        pipe_step<D, VI8, true, true, true, PH, PN>(krd + 32 * L::KSTR, vrd + 32 * L::VSTR, qreg, magic, sB, sA, pB,
-                                                    pA, O, m_run, l_run, qc * t1.kscale, t1.pscale, klane, vlane, hh,
+                                                   qc * t0.kscale, t0.pscale, lo, hh, cp);
+        pipe_step<D, VI8, true, true, true, PH, PN>(krd + 32 * L::KROW, vrd + 32 * L::VROW, qreg, magic, sB, sA, pB,
+                                                    pA, O, m_run, l_run, qc * t1.kscale, t1.pscale, lo, hh,
                                                     cp);
         if (VI8) store_v_int8<D>(vwr, vr, tid);
         t0 = t1;
@@ -690,18 +719,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       copies_done_barrier();
       const uint8_t* vl = (T & 1) ? vst1 : vst0;
       pipe_step<D, VI8, false, true, true, 0, 0>(kst0, vl, qreg, magic, sA, sB, pA, pB, O, m_run, l_run,
-                                                 qc * t0.kscale, t0.pscale, klane, vlane, hh, TileCopy<D, VI8>{});
-      half_pv<D>(vl, 32, pB, O, vlane);
+                                                 qc * t0.kscale, t0.pscale, lo, hh, TileCopy<D, VI8>{});
+      half_pv<D>(vl, 32, pB, O, lo);
     }
     copies_done_barrier();                       // stages free again
     for (int pi = 0; pi < nP; ++pi) {            // tiles with the end of a segment's valid keys
       const TileInfo t = fetch_tile<VI8>(a, bh, plist[pi], nKS, nVS);
       const int nvalid = pvalid[pi];
       if (VI8) load_v_int8<D>(v8base + (int64_t)t.vrow0() * D, vr, tid);
-      tile_copy<D, VI8>(t, t, kst0, vst0, sink, krs, vrs, plan, wave).all();
+      tile_copy<D, VI8>(t, t, kst0, vst0, krs, vrs, plan, wave).all();
       if (VI8) store_v_int8<D>(vst0, vr, tid);
       copies_done_barrier();
-      masked_tile<D, VI8>(kst0, vst0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, nvalid, klane, vlane, hh);
+      masked_tile<D, VI8>(kst0, vst0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, nvalid, lo, hh);
       __syncthreads();
     }
 
@@ -747,10 +776,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             vhi[e2] = (__bf16)vx;
             vlo[e2] = (__bf16)(vx - (float)vhi[e2]);
           }
-          *reinterpret_cast<v4bf*>(vst0 + col * L::KCSTR + c4 * 8) = khi;
-          *reinterpret_cast<v4bf*>(vst0 + L::KCL_OFF + col * L::KCSTR + c4 * 8) = klo;
-          *reinterpret_cast<v4bf*>(vst1 + col * L::VSTR + c4 * 8) = vhi;
-          *reinterpret_cast<v4bf*>(vst1 + L::VCL_OFF + col * L::VSTR + c4 * 8) = vlo;
+          *reinterpret_cast<v4bf*>(vst0 + L::kc_off(col, c4 * 8)) = khi;
+          *reinterpret_cast<v4bf*>(vst0 + L::KCL_OFF + L::kc_off(col, c4 * 8)) = klo;
+          *reinterpret_cast<v4bf*>(vst1 + L::v_off(col, c4 * 8)) = vhi;
+          *reinterpret_cast<v4bf*>(vst1 + L::VCL_OFF + L::v_off(col, c4 * 8)) = vlo;
         }
         if (q == 0) bias[col] = has ? __log2f(cn) : -INFINITY;
       }
@@ -761,7 +790,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const v8bf qb = i8x8_to_bf16(qreg[s][2 * pp], qreg[s][2 * pp + 1]);
-          const int off = n * L::KCSTR + (s * 32 + hh * 16 + pp * 8) * 2;
+          const int off = L::kc_off(n, (s * 32 + hh * 16 + pp * 8) * 2);
           const v8bf khi = *reinterpret_cast<const v8bf*>(vst0 + off);
           const v8bf klo = *reinterpret_cast<const v8bf*>(vst0 + L::KCL_OFF + off);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb, acc, 0, 0, 0);
@@ -796,10 +825,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NS; ++cb) {
           const int col = cb * 32 + (g16 & 1) * 16 + 4 * (j16 & 3);
-          const uint8_t* ph = vst1 + krow * L::VSTR + col * 2;
-          const uint8_t* pl = vst1 + L::VCL_OFF + krow * L::VSTR + col * 2;
-          const v8bf vh = cat8(tr16(ph), tr16(ph + 8 * L::VSTR));
-          const v8bf vl = cat8(tr16(pl), tr16(pl + 8 * L::VSTR));
+          const int o0 = L::v_off(krow, col * 2), o8 = L::v_off(krow + 8, col * 2);
+          const v8bf vh = cat8(tr16(vst1 + o0), tr16(vst1 + o8));
+          const v8bf vl = cat8(tr16(vst1 + L::VCL_OFF + o0), tr16(vst1 + L::VCL_OFF + o8));
           O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pf, O[cb], 0, 0, 0);
           O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, pf, O[cb], 0, 0, 0);
         }
