@@ -311,7 +311,7 @@ def main():
                     "map_entries": int(bmap.size)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak_mixed, 2),
                      "unit": "TFLOP/s", "frac": round(achieved / peak_mixed, 4), "traffic": traffic,
-                     "kernel": ("sparse_attn_fwd_float (fwd_float_kernel<128,true>)" if args.qk_float
+                     "kernel": ("sparse_attn_fwd_float (fwd_kernel<128,true,false,true>)" if args.qk_float
                                 else "sparse_attn_fwd (fwd_kernel<128,false,true>)"),
                      "frac_of_int8_peak": round(achieved / PEAK_INT8, 4), "kernel_hash": khash},
         "hbm_kernels": {

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["abi.hip", "quantize.hip", "route.hip", "fwd.hip", "fwd_float.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "route.hip", "fwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -48,9 +48,9 @@ constexpr float kLazy = 8.0f;  // rescale O only when the row max grows by more 
 //    positions get their 64-byte segments XORed with different values.
 // Every row's data stays inside its own row, so a whole tile is one
 // contiguous run of 1 KiB copy chunks (no padding lanes).
-template <int D>
+template <int D, int KB = 1>
 struct FwdLds {
-  static constexpr int KROW = D;              // int8 K tile row (bytes)
+  static constexpr int KROW = KB * D;         // K tile row (bytes): int8 (KB = 1) or bf16 (KB = 2)
   static constexpr int VROW = 2 * D;          // bf16 V tile row (bytes)
   static constexpr int KCROW = 2 * D;         // bf16 centroid-K row (bytes)
   static constexpr int KU = KROW / 16;        // 16-byte units per K row = 1 KiB copies per K tile
@@ -131,10 +131,10 @@ __device__ __forceinline__ void maybe_rescale(float m_tile, float& m_run, float&
 // chunk, so the permuted row layout is produced by picking each lane's
 // source.  The per-lane source offsets do not depend on the tile and are
 // computed once; the tile offset is a scalar.
-template <int D>
+template <int D, int KB>
 struct DmaPlan {
-  static constexpr int KI = FwdLds<D>::KU / 4;   // K copies per wave
-  static constexpr int VI = FwdLds<D>::VU / 4;   // V copies per wave
+  static constexpr int KI = FwdLds<D, KB>::KU / 4;   // K copies per wave
+  static constexpr int VI = FwdLds<D, KB>::VU / 4;   // V copies per wave
   uint32_t koff[KI];   // unsigned: the copy uses a scalar base plus a 32-bit lane offset
   uint32_t voff[VI];
 };
@@ -142,17 +142,17 @@ struct DmaPlan {
 // Lane L of copy chunk c lands at byte 1024c + 16L of the stage; its source is
 // the 16 bytes the layout puts there (XOR is its own inverse, so the logical
 // unit is the stored one XORed with the row's value).
-template <int D>
-__device__ __forceinline__ DmaPlan<D> make_dma_plan(int wave, int lane) {
-  using L = FwdLds<D>;
-  DmaPlan<D> pl;
+template <int D, int KB>
+__device__ __forceinline__ DmaPlan<D, KB> make_dma_plan(int wave, int lane) {
+  using L = FwdLds<D, KB>;
+  DmaPlan<D, KB> pl;
 #pragma unroll
-  for (int t = 0; t < DmaPlan<D>::KI; ++t) {
+  for (int t = 0; t < DmaPlan<D, KB>::KI; ++t) {
     const int pos = (wave + 4 * t) * 1024 + 16 * lane, row = pos / L::KROW;
     pl.koff[t] = (uint32_t)(row * L::KROW + (L::k_off(row, pos % L::KROW) - row * L::KROW));
   }
 #pragma unroll
-  for (int t = 0; t < DmaPlan<D>::VI; ++t) {
+  for (int t = 0; t < DmaPlan<D, KB>::VI; ++t) {
     const int pos = (wave + 4 * t) * 1024 + 16 * lane, row = pos / L::VROW;
     pl.voff[t] = (uint32_t)(row * L::VROW + (L::v_off(row, pos % L::VROW) - row * L::VROW));
   }
@@ -224,13 +224,13 @@ struct TileInfo {
   __device__ __forceinline__ int vrow0() const { return __builtin_amdgcn_readfirstlane(vsrc); }
 };
 
-template <bool VI8>
+template <bool QF, bool VI8>
 __device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int kt, int nKS, int nVS) {
   TileInfo t;
   t.krow0 = kt * kTile;
   t.vsrc = a.v_block_src ? min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile : t.krow0;
   if (VI8) t.vsrc = __builtin_amdgcn_readfirstlane(t.vsrc);   // the V scale index needs it now
-  t.kscale = a.k_scale[bh * nKS + t.krow0 / a.k_scale_rows];
+  t.kscale = QF ? 1.0f : a.k_scale[bh * nKS + t.krow0 / a.k_scale_rows];
   t.pscale = VI8 ? a.v_scale[bh * nVS + t.vsrc / a.v_scale_rows] : 1.0f;
   return t;
 }
@@ -245,15 +245,15 @@ __device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int
 // branch-free (wave is wave-uniform, every wave owns the same number of
 // chunks), so the pieces do not split the compute into separately scheduled
 // blocks.
-template <int D, bool VI8>
+template <int D, int KB, bool VI8>
 struct TileCopy {
-  static constexpr int KI = DmaPlan<D>::KI;
-  static constexpr int VI = VI8 ? 0 : DmaPlan<D>::VI;
+  static constexpr int KI = DmaPlan<D, KB>::KI;
+  static constexpr int VI = VI8 ? 0 : DmaPlan<D, KB>::VI;
   static constexpr int PIECES = KI + VI;   // direct loads per wave for one K tile and one V tile
   __amdgpu_buffer_rsrc_t krs, vrs;   // K (int8) and bf16 V of this head
   uint32_t koff, voff;               // byte offsets of the K tile's / V tile's first row
   uint32_t klds, vlds;               // destination K and V stages (LDS byte addresses)
-  const DmaPlan<D>* plan;
+  const DmaPlan<D, KB>* plan;
   int wave;                          // wave-uniform, 0..3
   __device__ __forceinline__ void k(int u) const {
     lds_dma16(krs, plan->koff[u], koff, klds + (wave + 4 * u) * 1024);
@@ -278,13 +278,14 @@ struct TileCopy {
 
 // Copy of the K tile of tk and the V tile of tv (bf16 V only) into the given
 // stages.
-template <int D, bool VI8>
-__device__ __forceinline__ TileCopy<D, VI8> tile_copy(const TileInfo& tk, const TileInfo& tv, uint8_t* kbuf,
-                                                      uint8_t* vbuf, __amdgpu_buffer_rsrc_t krs,
-                                                      __amdgpu_buffer_rsrc_t vrs, const DmaPlan<D>& plan, int wave) {
-  return TileCopy<D, VI8>{krs,
+template <int D, int KB, bool VI8>
+__device__ __forceinline__ TileCopy<D, KB, VI8> tile_copy(const TileInfo& tk, const TileInfo& tv, uint8_t* kbuf,
+                                                          uint8_t* vbuf, __amdgpu_buffer_rsrc_t krs,
+                                                          __amdgpu_buffer_rsrc_t vrs, const DmaPlan<D, KB>& plan,
+                                                          int wave) {
+  return TileCopy<D, KB, VI8>{krs,
                           vrs,
-                          (uint32_t)(tk.krow0 * D),
+                          (uint32_t)(tk.krow0 * KB * D),
                           (uint32_t)(tv.vrow0() * D * 2),
                           lds_address(kbuf),
                           lds_address(vbuf),
@@ -309,20 +310,45 @@ constexpr float kMagicF = 12582912.0f;
 // most this, so every weight stays far from fp32/bf16 overflow).
 constexpr float kFastSum = 4096.0f;
 
+// Score accumulators: int32 for the INT8 products (seeded with kMagicI, read
+// as float), fp32 for the floating ones.
+template <bool QF>
+struct ScoreAcc {
+  using type = v16i;
+};
+template <>
+struct ScoreAcc<true> {
+  using type = v16f;
+};
+template <bool QF>
+using SAcc = typename ScoreAcc<QF>::type;
+
+// Score e of a half as the float the weight FMA takes: 1.5*2^23 + S for the
+// INT8 products, the fp32 dot for the floating ones.
+__device__ __forceinline__ float score_f(const v16i& acc, int e) { return __int_as_float(acc[e]); }
+__device__ __forceinline__ float score_f(const v16f& acc, int e) { return acc[e]; }
+
+// The addend of the weight FMA, exp2(x*c + b) = exp2(S*c - m): it absorbs the
+// 1.5*2^23 offset of the INT8 scores.
+template <bool QF>
+__device__ __forceinline__ float weight_bias(float c, float m) {
+  return QF ? -m : -__builtin_fmaf(kMagicF, c, m);
+}
+
 // p = exp2(S*c - m) for the 16 scores a lane holds in one 32-key half of the
-// tile, as bf16 pairs (INT8 V: scaled by the V block scale before rounding).
-// x = 1.5*2^23 + S, and b = -(1.5*2^23*c + m) is formed once per row, so each
-// weight is one FMA and one exp2.  Returns the lane's row-sum part: the
-// bf16-rounded weights (bf16 V) or the unrounded unscaled ones (INT8 V).
-template <bool VI8, bool MASKED>
-__device__ __forceinline__ float half_weights(const v16i& acc, int key0, float c, float b, float pscale, int nvalid,
+// tile, as bf16 pairs (INT8 V: scaled by the V block scale before rounding);
+// b = weight_bias(c, m) is formed once per row, so each weight is one FMA and
+// one exp2.  Returns the lane's row-sum part: the bf16-rounded weights (bf16
+// V) or the unrounded unscaled ones (INT8 V).
+template <bool VI8, bool MASKED, class Acc>
+__device__ __forceinline__ float half_weights(const Acc& acc, int key0, float c, float b, float pscale, int nvalid,
                                               int hh, uint32_t (&pw)[8]) {
   typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
   float psum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[2 * e]), c, b));
-    float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[2 * e + 1]), c, b));
+    float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(score_f(acc, 2 * e), c, b));
+    float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(score_f(acc, 2 * e + 1), c, b));
     if (MASKED) {
       const int k0 = key0 + ((2 * e) / 4) * 8 + hh * 4 + (2 * e) % 4;
       p0 = k0 < nvalid ? p0 : 0.0f;
@@ -356,17 +382,29 @@ __device__ __forceinline__ float half_max(const v16i& acc, int key0, float c, in
   mi = max((int)r[0], (int)r[1]);
   return mi == INT_MIN ? -INFINITY : (float)(mi - kMagicI) * c;
 }
+template <bool MASKED>
+__device__ __forceinline__ float half_max(const v16f& acc, int key0, float c, int nvalid, int hh) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float v = acc[e];
+    if (MASKED) v = key0 + (e / 4) * 8 + hh * 4 + (e % 4) < nvalid ? v : -INFINITY;
+    mx = fmaxf(mx, v);
+  }
+  mx = pair_max(mx);
+  return mx == -INFINITY ? -INFINITY : mx * c;
+}
 
 // Exact online-softmax step for one 32-key half: the half's row max moves
 // m_run lazily, then the weights are computed against it.  Returns the lane's
 // row-sum part.
-template <int NS, bool VI8, bool MASKED>
-__device__ __forceinline__ float half_exact(const v16i& acc, int key0, float c, float pscale, int nvalid, int hh,
+template <int NS, bool VI8, bool MASKED, bool QF>
+__device__ __forceinline__ float half_exact(const SAcc<QF>& acc, int key0, float c, float pscale, int nvalid, int hh,
                                             v16f (&O)[NS], float& m_run, float& l_run, uint32_t (&pw)[8]) {
   maybe_rescale<NS>(half_max<MASKED>(acc, key0, c, nvalid, hh), m_run, l_run, O);
   // rows with no valid key so far keep m_run = -inf; their weights are 0
   const float m = m_run == -INFINITY ? 0.0f : m_run;
-  return half_weights<VI8, MASKED>(acc, key0, c, -__builtin_fmaf(kMagicF, c, m), pscale, nvalid, hh, pw);
+  return half_weights<VI8, MASKED>(acc, key0, c, weight_bias<QF>(c, m), pscale, nvalid, hh, pw);
 }
 
 // Fast-path acceptance: every lane's partial row sum is finite and at most
@@ -374,28 +412,29 @@ __device__ __forceinline__ float half_exact(const v16i& acc, int key0, float c, 
 __device__ __forceinline__ bool fast_ok(float psum) { return __ballot(!(psum <= kFastSum)) == 0; }
 
 // Per-lane LDS offsets of the tile readers (their layout terms depend only on
-// the lane): k[x], the K operand of k-step x (row n, bytes 32x + 16hh);
-// v[c], the V^T operand for output block c (rows hh*4 + j16/4 (+8),
-// bytes 64c + (g16&1)*32 + (j16&3)*8 of the row).
-template <int D>
+// the lane): k[x], the K operand of k-step x (row n, bytes 32x + 16hh: 16
+// int8 or 8 bf16 channels); v[c], the V^T operand for output block c (rows
+// hh*4 + j16/4 (+8), bytes 64c + (g16&1)*32 + (j16&3)*8 of the row).
+template <int D, int KB>
 struct LaneOffsets {
-  int k[D / 32];
+  static constexpr int KS = KB * D / 32;   // QK k-steps per half
+  int k[KS];
   int v[D / 32];
 };
 
 // O^T += V^T.P^T for one 32-key half (two k-steps of 16 keys).
-template <int D>
+template <int D, int KB>
 __device__ __forceinline__ void half_pv(const uint8_t* vbuf, int key0, const uint32_t (&pw)[8], v16f (&O)[D / 32],
-                                        const LaneOffsets<D>& lo);
+                                        const LaneOffsets<D, KB>& lo);
 
 // One weight pair (scores 2e, 2e+1 of a half) on the fast path: two FMAs, two
 // exp2, one bf16 pack and the row-sum update.
-template <bool VI8>
-__device__ __forceinline__ void weight_pair(const v16i& acc, int e, float c, float b, float pscale, float& psum,
+template <bool VI8, class Acc>
+__device__ __forceinline__ void weight_pair(const Acc& acc, int e, float c, float b, float pscale, float& psum,
                                             uint32_t (&pw)[8]) {
   typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[2 * e]), c, b));
-  const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[2 * e + 1]), c, b));
+  const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(score_f(acc, 2 * e), c, b));
+  const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(score_f(acc, 2 * e + 1), c, b));
   v2bf pk;
   if (VI8) {
     psum += p0 + p1;
@@ -408,8 +447,8 @@ __device__ __forceinline__ void weight_pair(const v16i& acc, int e, float c, flo
 }
 
 // V^T operand of PV MFMA i (k-step i / NS of the half, output block i % NS).
-template <int D>
-__device__ __forceinline__ v8bf v_frag(const uint8_t* vbuf, int key0, int i, const LaneOffsets<D>& lo) {
+template <int D, int KB>
+__device__ __forceinline__ v8bf v_frag(const uint8_t* vbuf, int key0, int i, const LaneOffsets<D, KB>& lo) {
   using L = FwdLds<D>;
   constexpr int NS = D / 32;
   const uint8_t* p0 = vbuf + lo.v[i % NS] + (key0 + (i / NS) * 16) * L::VROW;
@@ -424,14 +463,36 @@ __device__ __forceinline__ v8bf p_frag(const uint32_t (&pw)[8], int i) {
   return __builtin_bit_cast(v8bf, pwv);
 }
 
-template <int D>
+template <int D, int KB>
 __device__ __forceinline__ void half_pv(const uint8_t* vbuf, int key0, const uint32_t (&pw)[8], v16f (&O)[D / 32],
-                                        const LaneOffsets<D>& lo) {
+                                        const LaneOffsets<D, KB>& lo) {
   constexpr int NS = D / 32;
 #pragma unroll
   for (int i = 0; i < 2 * NS; ++i)
-    O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(vbuf, key0, i, lo), p_frag<D>(pw, i), O[i % NS],
+    O[i % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, KB>(vbuf, key0, i, lo), p_frag<D>(pw, i), O[i % NS],
                                                         0, 0, 0);
+}
+
+// The query fragment, the B operand of S^T = K.Q^T: lane (n, hh) holds query
+// row n of its wave, channels 32s + 16hh .. +15 (int8) or 16s + 8hh .. +7
+// (bf16) of k-step s.
+template <int D, bool QF>
+struct QFrag {
+  v4i q[D / 32];
+};
+template <int D>
+struct QFrag<D, true> {
+  v8bf q[D / 16];
+};
+
+// One QK^T k-step: acc (+)= K_tile_rows . Q^T over the step's channels.
+template <int D>
+__device__ __forceinline__ v16i qk_mfma(v4i kop, const QFrag<D, false>& qf, int x, const v16i& acc) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qf.q[x], acc, 0, 0, 0);
+}
+template <int D>
+__device__ __forceinline__ v16f qk_mfma(v4i kop, const QFrag<D, true>& qf, int x, const v16f& acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kop), qf.q[x], acc, 0, 0, 0);
 }
 
 // The exact 64-key tiles, as a software pipeline over 32-key halves.
@@ -472,24 +533,25 @@ __device__ constexpr int step_index(int m) {
 // whose weights go to p_cur (DO_W), with their row-sum part added to l_run
 // after the fast-path check.  The copy pieces [P0, P1) of cp are issued in
 // between.
-template <int D, bool VI8, bool DO_QK, bool DO_PV, bool DO_W, int P0, int P1>
-__device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, const v4i (&qreg)[D / 32],
-                                          const v16i& magic, v16i& s_next, const v16i& s_cur,
+template <int D, bool QF, bool VI8, bool DO_QK, bool DO_PV, bool DO_W, int P0, int P1>
+__device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, const QFrag<D, QF>& qf,
+                                          const SAcc<QF>& seed, SAcc<QF>& s_next, const SAcc<QF>& s_cur,
                                           const uint32_t (&p_prev)[8], uint32_t (&p_cur)[8], v16f (&O)[D / 32],
                                           float& m_run, float& l_run, float c, float pscale,
-                                          const LaneOffsets<D>& lo, int hh, const TileCopy<D, VI8>& cp) {
-  constexpr int NS = D / 32;
-  constexpr int NQ = DO_QK ? NS : 0, NP = DO_PV ? 2 * NS : 0, M = NQ + NP, NC = P1 - P0;
+                                          const LaneOffsets<D, QF ? 2 : 1>& lo, int hh,
+                                          const TileCopy<D, QF ? 2 : 1, VI8>& cp) {
+  constexpr int NS = D / 32, KS = LaneOffsets<D, QF ? 2 : 1>::KS;
+  constexpr int NQ = DO_QK ? KS : 0, NP = DO_PV ? 2 * NS : 0, M = NQ + NP, NC = P1 - P0;
   static_assert(M > 0, "a step issues matrix work");
   // A operands, loaded two MFMAs ahead (K rows: 16 int8 channels; V^T: 8 bf16)
   v4i op[M];
   auto load = [&](int m) {
     const int x = step_index<NQ, NP>(m);
     if (step_is_qk<NQ, NP>(m)) op[m] = *reinterpret_cast<const v4i*>(kh + lo.k[x]);
-    else op[m] = __builtin_bit_cast(v4i, v_frag<D>(vh, 0, x, lo));
+    else op[m] = __builtin_bit_cast(v4i, v_frag<D, QF ? 2 : 1>(vh, 0, x, lo));
   };
   float ps = 0.0f;
-  const float b = -__builtin_fmaf(kMagicF, c, m_run);
+  const float b = weight_bias<QF>(c, m_run);
   load(0);
   if (M > 1) load(1);
   __builtin_amdgcn_sched_barrier(0);
@@ -497,7 +559,7 @@ __device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, 
   for (int m = 0; m < M; ++m) {
     const int x = step_index<NQ, NP>(m);
     if (step_is_qk<NQ, NP>(m))
-      s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(op[m], qreg[x], x == 0 ? magic : s_next, 0, 0, 0);
+      s_next = qk_mfma<D>(op[m], qf, x, x == 0 ? seed : s_next);
     else
       O[x % NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, op[m]), p_frag<D>(p_prev, x),
                                                           O[x % NS], 0, 0, 0);
@@ -513,40 +575,46 @@ __device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, 
     __builtin_amdgcn_sched_barrier(0);
   }
   if (DO_W) {
-    if (!fast_ok(ps)) ps = half_exact<NS, VI8, false>(s_cur, 0, c, pscale, kTile, hh, O, m_run, l_run, p_cur);
+    if (!fast_ok(ps)) ps = half_exact<NS, VI8, false, QF>(s_cur, 0, c, pscale, kTile, hh, O, m_run, l_run, p_cur);
     l_run += ps;
   }
 }
 
 // The tile holding the end of a segment's valid keys (keys >= nvalid drop),
 // done on its own with the exact step for both halves.
-template <int D, bool VI8>
-__device__ __forceinline__ void masked_tile(const uint8_t* kbuf, const uint8_t* vbuf, const v4i (&qreg)[D / 32],
-                                            const v16i& magic, v16f (&O)[D / 32], float& m_run, float& l_run,
-                                            float c, float pscale, int nvalid, const LaneOffsets<D>& lo, int hh) {
-  using L = FwdLds<D>;
-  constexpr int NS = D / 32;
-  v16i acc0 = magic, acc1 = magic;
+template <int D, bool QF, bool VI8>
+__device__ __forceinline__ void masked_tile(const uint8_t* kbuf, const uint8_t* vbuf, const QFrag<D, QF>& qf,
+                                            const SAcc<QF>& seed, v16f (&O)[D / 32], float& m_run, float& l_run,
+                                            float c, float pscale, int nvalid, const LaneOffsets<D, QF ? 2 : 1>& lo,
+                                            int hh) {
+  constexpr int KB = QF ? 2 : 1;
+  using L = FwdLds<D, KB>;
+  constexpr int NS = D / 32, KS = LaneOffsets<D, KB>::KS;
+  SAcc<QF> acc0 = seed, acc1 = seed;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(kbuf + lo.k[s]), qreg[s], acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(kbuf + 32 * L::KROW + lo.k[s]), qreg[s],
-                                                 acc1, 0, 0, 0);
+  for (int s = 0; s < KS; ++s) {
+    acc0 = qk_mfma<D>(*reinterpret_cast<const v4i*>(kbuf + lo.k[s]), qf, s, acc0);
+    acc1 = qk_mfma<D>(*reinterpret_cast<const v4i*>(kbuf + 32 * L::KROW + lo.k[s]), qf, s, acc1);
   }
   uint32_t pw0[8], pw1[8];
-  l_run += half_exact<NS, VI8, true>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
-  half_pv<D>(vbuf, 0, pw0, O, lo);
-  l_run += half_exact<NS, VI8, true>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
-  half_pv<D>(vbuf, 32, pw1, O, lo);
+  l_run += half_exact<NS, VI8, true, QF>(acc0, 0, c, pscale, nvalid, hh, O, m_run, l_run, pw0);
+  half_pv<D, KB>(vbuf, 0, pw0, O, lo);
+  l_run += half_exact<NS, VI8, true, QF>(acc1, 32, c, pscale, nvalid, hh, O, m_run, l_run, pw1);
+  half_pv<D, KB>(vbuf, 32, pw1, O, lo);
 }
 
 
 }  // namespace
 
-template <int D, bool VI8, bool OBF16>
+// QF: the exact tiles' QK^T on bf16 Q/K (fp32 scores) instead of the INT8
+// codes; routing, centroids and everything after the scores are shared.
+template <int D, bool QF, bool VI8, bool OBF16>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  using L = FwdLds<D>;
-  constexpr int NS = D / 32;   // int8 k-steps of 32 channels; also 32-channel output blocks
+  constexpr int KB = QF ? 2 : 1;   // bytes per K element
+  using L = FwdLds<D, KB>;
+  constexpr int NS = D / 32;       // 32-channel output blocks
+  constexpr int KS = LaneOffsets<D, KB>::KS;
+  static_assert(!(QF && VI8), "the floating path takes bf16 V");
   // Two K and two V stages as separate LDS objects, so the compiler can see
   // that reading one stage does not depend on the direct loads into another.
   __shared__ __attribute__((aligned(16))) uint8_t kst0[L::KST];
@@ -562,14 +630,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __builtin_assume(wave >= 0 && wave < 4);
   const int n = lane & 31, hh = lane >> 5;
   // per-lane LDS offsets of the tile readers (see LaneOffsets)
-  LaneOffsets<D> lo;
+  LaneOffsets<D, KB> lo;
   {
     const int vq = hh * 4 + ((lane & 15) >> 2);
 #pragma unroll
-    for (int x = 0; x < NS; ++x) {
-      lo.k[x] = opaque(L::k_off(n, 32 * x + 16 * hh));
-      lo.v[x] = opaque(L::v_off(vq, 64 * x + ((lane >> 4) & 1) * 32 + (lane & 3) * 8));
-    }
+    for (int x = 0; x < KS; ++x) lo.k[x] = opaque(L::k_off(n, 32 * x + 16 * hh));
+#pragma unroll
+    for (int x = 0; x < NS; ++x) lo.v[x] = opaque(L::v_off(vq, 64 * x + ((lane >> 4) & 1) * 32 + (lane & 3) * 8));
   }
 
   // XCD-aware block order: hardware id b runs on XCD b % 8; give each XCD a
@@ -579,41 +646,51 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   if ((nwg & 7) == 0) bid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
   const int i = bid % a.nQB;
   const int64_t bh = bid / a.nQB;
-  const int nKS = a.Lkv / a.k_scale_rows;
+  const int nKS = QF ? 1 : a.Lkv / a.k_scale_rows;
   const int nVS = VI8 ? a.Lv / a.v_scale_rows : 1;
   const int tpb = a.kblock / kTile;   // 64-key tiles per key block
 
-  // Q fragment (B operand of S^T = K.Q^T): lane holds query row n of this
-  // wave, channels s*32 + hh*16 .. +15 for each k-step s.
+  // Q fragment (B operand of S^T = K.Q^T), see QFrag.
   const int qrow = i * kQBlock + wave * 32 + n;
-  v4i qreg[NS];
-  {
+  QFrag<D, QF> qf;
+  if constexpr (QF) {
+    const uint16_t* qp = a.qb + (bh * a.Lq + qrow) * D + hh * 8;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf.q[s] = *reinterpret_cast<const v8bf*>(qp + s * 16);
+  } else {
     const int8_t* qp = a.q + (bh * a.Lq + qrow) * D + hh * 16;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const v4i*>(qp + s * 32);
+    for (int s = 0; s < KS; ++s) qf.q[s] = *reinterpret_cast<const v4i*>(qp + s * 32);
   }
-  const float qc = a.q_scale[bh * a.nQB + i] * a.sm_log2;
+  // logit scale: c = qc * (K block scale) for the INT8 scores, qc for fp32 ones
+  const float qc = QF ? a.sm_log2 : a.q_scale[bh * a.nQB + i] * a.sm_log2;
 
-  // Initial value of the integer score accumulators (see kMagicI), built once:
-  // the empty asm keeps it in registers instead of re-creating it per tile.
-  v16i magic;
+  // Initial value of the score accumulators: zero for fp32 scores; for the
+  // INT8 ones the bit pattern kMagicI, built once (the empty asm keeps it in
+  // registers instead of re-creating it per tile).
+  SAcc<QF> seed;
+  if constexpr (QF) {
+    seed = (v16f){};
+  } else {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) magic[e] = kMagicI;
-  asm volatile("" : "+v"(magic));
+    for (int e = 0; e < 16; ++e) seed[e] = kMagicI;
+    asm volatile("" : "+v"(seed));
+  }
   v16f O[NS];
 #pragma unroll
   for (int c = 0; c < NS; ++c) O[c] = (v16f){};
   float m_run = -INFINITY, l_run = 0.0f;
   const uint8_t* mrow = a.map + (bh * a.nQB + i) * a.nKB;
-  const int8_t* kbase = a.k + bh * a.Lkv * D;
+  const uint8_t* kbase = QF ? reinterpret_cast<const uint8_t*>(a.kb + bh * a.Lkv * D)
+                            : reinterpret_cast<const uint8_t*>(a.k + bh * a.Lkv * D);
   const int8_t* v8base = static_cast<const int8_t*>(a.v) + bh * a.Lv * D;
   const uint8_t* v16base = static_cast<const uint8_t*>(a.v) + bh * a.Lv * D * 2;
   // buffer resources over this head's K and bf16 V (the tile copies); the
   // per-head sizes fit 32 bits (checked when the call is validated)
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kbase, (uint32_t)((int64_t)a.Lkv * D));
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kbase, (uint32_t)((int64_t)a.Lkv * D * KB));
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v16base, VI8 ? 0u : (uint32_t)((int64_t)a.Lv * D * 2));
   VRegs<D> vr;
-  const DmaPlan<D> plan = make_dma_plan<D>(wave, lane);
+  const DmaPlan<D, KB> plan = make_dma_plan<D, KB>(wave, lane);
 
   for (int w0 = 0; w0 < a.nKB; w0 += kWin) {
     const int wend = min(a.nKB, w0 + kWin);
@@ -666,23 +743,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // repeats tile T+1 into the free stage, which nothing reads.
     // Registers: scores of even halves sA, odd halves sB; weights pA / pB.
     if (nE > 0) {
-      constexpr int PH = (TileCopy<D, VI8>::PIECES + 1) / 2;   // copy pieces in a tile's first step
-      constexpr int PN = TileCopy<D, VI8>::PIECES;
-      TileInfo t0 = fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS);
-      TileInfo t1 = nE > 1 ? fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[1]), nKS, nVS) : t0;
+      constexpr int PH = (TileCopy<D, KB, VI8>::PIECES + 1) / 2;   // copy pieces in a tile's first step
+      constexpr int PN = TileCopy<D, KB, VI8>::PIECES;
+      TileInfo t0 = fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS);
+      TileInfo t1 = nE > 1 ? fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[1]), nKS, nVS) : t0;
       if (VI8) load_v_int8<D>(v8base + (int64_t)t0.vrow0() * D, vr, tid);
-      tile_copy<D, VI8>(t0, t0, kst0, vst0, krs, vrs, plan, wave).all();
-      tile_copy<D, VI8>(t1, t1, kst1, vst1, krs, vrs, plan, wave).all_k();
+      tile_copy<D, KB, VI8>(t0, t0, kst0, vst0, krs, vrs, plan, wave).all();
+      tile_copy<D, KB, VI8>(t1, t1, kst1, vst1, krs, vrs, plan, wave).all_k();
       if (VI8) store_v_int8<D>(vst0, vr, tid);
       copies_done_barrier();
-      v16i sA, sB;
+      SAcc<QF> sA, sB;
       uint32_t pA[8], pB[8];
       // step 0: scores of half 0 first, then half 1's with half 0's weights
-      pipe_step<D, VI8, true, false, false, 0, 0>(kst0, vst0, qreg, magic, sA, sB, pB, pA, O, m_run, l_run, 0.0f, 0.0f,
-                                                  lo, hh, TileCopy<D, VI8>{});
-      pipe_step<D, VI8, true, false, true, 0, 0>(kst0 + 32 * L::KROW, vst0, qreg, magic, sB, sA, pB, pA, O, m_run,
+      pipe_step<D, QF, VI8, true, false, false, 0, 0>(kst0, vst0, qf, seed, sA, sB, pB, pA, O, m_run, l_run, 0.0f, 0.0f,
+                                                  lo, hh, TileCopy<D, KB, VI8>{});
+      pipe_step<D, QF, VI8, true, false, true, 0, 0>(kst0 + 32 * L::KROW, vst0, qf, seed, sB, sA, pB, pA, O, m_run,
                                                  l_run, qc * t0.kscale, t0.pscale, lo, hh,
-                                                 TileCopy<D, VI8>{});
+                                                 TileCopy<D, KB, VI8>{});
       // Tile iteration T (T + 1 < nE), between the barrier that opens it and
       // the next one: steps 2T+1 and 2T+2.  ODD is T's parity, which picks the
       // stages at compile time.
@@ -694,13 +771,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         uint8_t* const vwr = ODD ? vst0 : vst1;   // V of tile T+1 goes here
         copies_done_barrier();
         const TileInfo t2 =
-            T + 2 < nE ? fetch_tile<VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[T + 2]), nKS, nVS)
+            T + 2 < nE ? fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[T + 2]), nKS, nVS)
                        : t1;
         if (VI8) load_v_int8<D>(v8base + (int64_t)t1.vrow0() * D, vr, tid);
-        const TileCopy<D, VI8> cp = tile_copy<D, VI8>(t2, t1, kwr, vwr, krs, vrs, plan, wave);
-        pipe_step<D, VI8, true, true, true, 0, PH>(krd, vrd, qreg, magic, sA, sB, pA, pB, O, m_run, l_run,
+        const TileCopy<D, KB, VI8> cp = tile_copy<D, KB, VI8>(t2, t1, kwr, vwr, krs, vrs, plan, wave);
+        pipe_step<D, QF, VI8, true, true, true, 0, PH>(krd, vrd, qf, seed, sA, sB, pA, pB, O, m_run, l_run,
                                                    qc * t0.kscale, t0.pscale, lo, hh, cp);
-        pipe_step<D, VI8, true, true, true, PH, PN>(krd + 32 * L::KROW, vrd + 32 * L::VROW, qreg, magic, sB, sA, pB,
+        pipe_step<D, QF, VI8, true, true, true, PH, PN>(krd + 32 * L::KROW, vrd + 32 * L::VROW, qf, seed, sB, sA, pB,
                                                     pA, O, m_run, l_run, qc * t1.kscale, t1.pscale, lo, hh,
                                                     cp);
         if (VI8) store_v_int8<D>(vwr, vr, tid);
@@ -718,19 +795,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       // at run time)
       copies_done_barrier();
       const uint8_t* vl = (T & 1) ? vst1 : vst0;
-      pipe_step<D, VI8, false, true, true, 0, 0>(kst0, vl, qreg, magic, sA, sB, pA, pB, O, m_run, l_run,
-                                                 qc * t0.kscale, t0.pscale, lo, hh, TileCopy<D, VI8>{});
-      half_pv<D>(vl, 32, pB, O, lo);
+      pipe_step<D, QF, VI8, false, true, true, 0, 0>(kst0, vl, qf, seed, sA, sB, pA, pB, O, m_run, l_run,
+                                                 qc * t0.kscale, t0.pscale, lo, hh, TileCopy<D, KB, VI8>{});
+      half_pv<D, KB>(vl, 32, pB, O, lo);
     }
     copies_done_barrier();                       // stages free again
     for (int pi = 0; pi < nP; ++pi) {            // tiles with the end of a segment's valid keys
-      const TileInfo t = fetch_tile<VI8>(a, bh, plist[pi], nKS, nVS);
+      const TileInfo t = fetch_tile<QF, VI8>(a, bh, plist[pi], nKS, nVS);
       const int nvalid = pvalid[pi];
       if (VI8) load_v_int8<D>(v8base + (int64_t)t.vrow0() * D, vr, tid);
-      tile_copy<D, VI8>(t, t, kst0, vst0, krs, vrs, plan, wave).all();
+      tile_copy<D, KB, VI8>(t, t, kst0, vst0, krs, vrs, plan, wave).all();
       if (VI8) store_v_int8<D>(vst0, vr, tid);
       copies_done_barrier();
-      masked_tile<D, VI8>(kst0, vst0, qreg, magic, O, m_run, l_run, qc * t.kscale, t.pscale, nvalid, lo, hh);
+      masked_tile<D, QF, VI8>(kst0, vst0, qf, seed, O, m_run, l_run, qc * t.kscale, t.pscale, nvalid, lo, hh);
       __syncthreads();
     }
 
@@ -784,18 +861,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         if (q == 0) bias[col] = has ? __log2f(cn) : -INFINITY;
       }
       __syncthreads();
+      // q . K-bar on bf16 MFMA: the INT8 query codes (exact in bf16; the query
+      // scale is in qc) or the bf16 query, against the hi and lo parts
       v16f acc = (v16f){};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const v8bf qb = i8x8_to_bf16(qreg[s][2 * pp], qreg[s][2 * pp + 1]);
-          const int off = L::kc_off(n, (s * 32 + hh * 16 + pp * 8) * 2);
-          const v8bf khi = *reinterpret_cast<const v8bf*>(vst0 + off);
-          const v8bf klo = *reinterpret_cast<const v8bf*>(vst0 + L::KCL_OFF + off);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qb, acc, 0, 0, 0);
+      for (int s = 0; s < D / 16; ++s) {
+        v8bf qb;
+        int ch;   // first channel of this lane's 8 in k-step s
+        if constexpr (QF) {
+          qb = qf.q[s];
+          ch = s * 16 + hh * 8;
+        } else {
+          qb = i8x8_to_bf16(qf.q[s / 2][2 * (s % 2)], qf.q[s / 2][2 * (s % 2) + 1]);
+          ch = (s / 2) * 32 + hh * 16 + (s % 2) * 8;
         }
+        const int off = L::kc_off(n, ch * 2);
+        const v8bf khi = *reinterpret_cast<const v8bf*>(vst0 + off);
+        const v8bf klo = *reinterpret_cast<const v8bf*>(vst0 + L::KCL_OFF + off);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qb, acc, 0, 0, 0);
       }
       float x[16];
       float mx = -INFINITY;
@@ -865,14 +949,47 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 template <int D, bool VI8>
 static hipError_t launch_fwd_dv(const FwdArgs& a, hipStream_t st) {
   dim3 grid(a.B * a.H * a.nQB);
-  if (a.out_bf16) fwd_kernel<D, VI8, true><<<grid, 256, 0, st>>>(a);
-  else fwd_kernel<D, VI8, false><<<grid, 256, 0, st>>>(a);
+  if (a.out_bf16) fwd_kernel<D, false, VI8, true><<<grid, 256, 0, st>>>(a);
+  else fwd_kernel<D, false, VI8, false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   if (a.d == 64) return a.v_int8 ? launch_fwd_dv<64, true>(a, st) : launch_fwd_dv<64, false>(a, st);
   return a.v_int8 ? launch_fwd_dv<128, true>(a, st) : launch_fwd_dv<128, false>(a, st);
+}
+
+// The floating path: the same kernel with bf16 Q/K (and bf16 V).
+template <int D>
+static hipError_t launch_fwd_float_d(const FwdArgs& a, hipStream_t st) {
+  dim3 grid(a.B * a.H * a.nQB);
+  if (a.out_bf16) fwd_kernel<D, true, false, true><<<grid, 256, 0, st>>>(a);
+  else fwd_kernel<D, true, false, false><<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_float(const FwdFloatArgs& f, hipStream_t st) {
+  FwdArgs a{};
+  a.qb = f.q;
+  a.kb = f.k;
+  a.v = f.v;
+  a.v_block_src = f.v_block_src;
+  a.map = f.map;
+  a.kc = f.kc;
+  a.vc = f.vc;
+  a.cnt = f.cnt;
+  a.out = f.out;
+  a.lse = f.lse;
+  a.B = f.B; a.H = f.H; a.Lq = f.Lq; a.Lkv = f.Lkv; a.Lv = f.Lv; a.d = f.d;
+  a.lq_valid = f.lq_valid; a.lkv_valid = f.lkv_valid;
+  a.nQB = f.nQB; a.nKB = f.nKB; a.kblock = f.kblock; a.G = f.G;
+  a.k_scale_rows = kTile;   // unused on this path (no K scales); kept non-zero
+  a.v_scale_rows = kTile;
+  a.lay = f.lay;
+  a.v_int8 = false;
+  a.out_bf16 = f.out_bf16;
+  a.sm_log2 = f.sm_log2;
+  return f.d == 64 ? launch_fwd_float_d<64>(a, st) : launch_fwd_float_d<128>(a, st);
 }
 
 }  // namespace sa

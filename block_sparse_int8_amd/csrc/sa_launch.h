@@ -98,6 +98,8 @@ struct FwdArgs {
   const float* q_scale;
   const int8_t* k;
   const float* k_scale;
+  const uint16_t* qb;   // floating path: bf16 Q [B,H,Lq,d] and K [B,H,Lkv,d] instead of q/k and their scales
+  const uint16_t* kb;
   const void* v;
   const float* v_scale;
   const int32_t* v_block_src;
