@@ -312,7 +312,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak_mixed, 2),
                      "unit": "TFLOP/s", "frac": round(achieved / peak_mixed, 4), "traffic": traffic,
                      "kernel": ("sparse_attn_fwd_float (fwd_kernel<128,true,false,true>)" if args.qk_float
-                                else "sparse_attn_fwd (fwd_kernel<128,false,true>)"),
+                                else "sparse_attn_fwd (fwd_kernel<128,false,false,true>)"),
                      "frac_of_int8_peak": round(achieved / PEAK_INT8, 4), "kernel_hash": khash},
         "hbm_kernels": {
             "quantize_qk_int8": {"bytes": quant_bytes,
