@@ -755,7 +755,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       SAcc<QF> sA, sB;
       uint32_t pA[8], pB[8];
       // step 0: scores of half 0 first, then half 1's with half 0's weights
-      pipe_step<D, QF, VI8, true, false, false, 0, 0>(kst0, vst0, qf, seed, sA, sB, pB, pA, O, m_run, l_run, 0.0f, 0.0f,
+      pipe_step<D, QF, VI8, true, false, false, 0, 0>(kst0, vst0, qf, seed, sA, seed, pB, pA, O, m_run, l_run, 0.0f, 0.0f,
                                                   lo, hh, TileCopy<D, KB, VI8>{});
       pipe_step<D, QF, VI8, true, false, true, 0, 0>(kst0 + 32 * L::KROW, vst0, qf, seed, sB, sA, pB, pA, O, m_run,
                                                  l_run, qc * t0.kscale, t0.pscale, lo, hh,
