@@ -5,7 +5,6 @@ import numpy as np
 import pytest
 import torch
 
-import workloads as W
 from workloads import bf16_bits, EXACT
 from tests.helpers import MAX_ABS, MEAN_ABS, bf16_dev, compare_outputs, say
 

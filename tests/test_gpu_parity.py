@@ -1,6 +1,5 @@
 """GPU parity: the HIP path (through the C ABI) against the oracle on the same
 seeded inputs.  Every test here needs an MI355X."""
-import math
 
 import numpy as np
 import pytest

@@ -7,7 +7,6 @@ cache is a ring of slabs; each new slab evicts the oldest.
 import numpy as np
 import pytest
 
-import workloads as W
 from workloads import bf16_bits
 
 

@@ -10,7 +10,6 @@ masked kernel is slower but correct, and is the intended fallback.
 import math
 
 import numpy as np
-import pytest
 import torch
 
 import workloads as W
