@@ -733,11 +733,15 @@ __global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
 // Fixed-sparsity decisions with LDS-resident proxies.  The keep-th largest
 // 96-bit key of a query block (the same keys as decide_topk_kernel) is found
 // bit by bit inside one wave: lane l holds candidates l, l+64, ... of the row
-// in registers, and each step counts, with one ballot per register, the keys
-// that match the prefix so far and have a 1 in the next bit.  If at least
-// `remaining` do, the bit is 1; otherwise it is 0 and those keys are all kept.
-// The row is settled when every key matching the prefix is kept (at bit 96 at
-// the latest, where one key matches).  No atomics and no barriers.
+// in registers, and each step counts the keys that match the prefix so far
+// and have a 1 in the next bit.  If at least `remaining` do, the bit is 1;
+// otherwise it is 0 and those keys are all kept.  The row is settled when
+// every key matching the prefix is kept (at bit 96 at the latest, where one
+// key matches).  Which of its candidates still match the prefix is one byte
+// per lane in a vector register, and a step's count is the lane's popcount
+// summed over the wave with one ballot per bit of it: the scalar unit, shared
+// by the CU's waves, issues a few instructions per step.  No atomics and no
+// barriers.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
   constexpr int NT = 64 * NW;
@@ -768,9 +772,10 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
     for (int r = wave; r < 32; r += NW) {
       if (i0 + r >= a.nQB) break;
       // the key of each register in three 32-bit words, most significant first;
-      // which lanes still match the prefix, one wave mask per register
+      // bit k of live: candidate k of this lane still matches the prefix
+      static_assert(NV <= 8, "the per-lane count must fit four bits");
       uint32_t w0[NV], w1[NV], w2[NV];
-      uint64_t live[NV];
+      uint32_t live = 0;
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int c = lane + 64 * k;
@@ -780,22 +785,22 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
         w0[k] = (uint32_t)(hk >> 32);
         w1[k] = (uint32_t)hk;
         w2[k] = ~(uint32_t)(cr.jc0 + c);
-        live[k] = __ballot(cand);
+        live |= cand ? 1u << k : 0u;
       }
       int m = N, rem = keep, nb = 0;
       uint64_t ph = 0;
       uint32_t pl = 0;
-      // one bit per step; the word is shifted so that the bit is its sign
-      auto phase = [&](uint32_t (&w)[NV]) __attribute__((always_inline)) {
+      // one bit per step, bit 31 - step of the word
+      auto phase = [&](const uint32_t (&w)[NV]) __attribute__((always_inline)) {
         for (int step = 0; step < 32 && m != rem; ++step, ++nb) {
-          uint64_t ones[NV];
+          uint32_t plane = 0;   // bit k: the step's bit of candidate k
+#pragma unroll
+          for (int k = 0; k < NV; ++k) plane |= ((w[k] >> (31 - step)) & 1u) << k;
+          const uint32_t ones = live & plane;
+          const uint32_t cnt = __builtin_popcount(ones);   // 0 .. NV
           int c1 = 0;
 #pragma unroll
-          for (int k = 0; k < NV; ++k) {
-            ones[k] = __ballot((int32_t)w[k] < 0) & live[k];
-            c1 += __popcll(ones[k]);
-            w[k] <<= 1;
-          }
+          for (int bit = 0; bit < 4; ++bit) c1 += __popcll(__ballot((cnt >> bit) & 1u)) << bit;
           const bool one = c1 >= rem;
           if (one) {
             m = c1;
@@ -803,8 +808,7 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
             rem -= c1;
             m -= c1;
           }
-#pragma unroll
-          for (int k = 0; k < NV; ++k) live[k] = one ? ones[k] : live[k] & ~ones[k];
+          live = one ? ones : live & ~plane;
           if (nb < 64) ph = (ph << 1) | (one ? 1ull : 0ull);
           else pl = (pl << 1) | (one ? 1u : 0u);
         }
