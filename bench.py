@@ -67,10 +67,11 @@ def read_traffic(expect_hash: str):
         return None
 
 
-def fwd_algorithmic_ops(bmap: np.ndarray, count: np.ndarray, d: int) -> float:
+def fwd_algorithmic_ops(bmap: np.ndarray, count: np.ndarray, d: int) -> tuple:
     """Ops the method itself performs in the forward kernel: per exact
     (128-query x 64-key) tile 2*128*64*d for QK^T and as many for PV; per
-    centroid column with a non-zero count 2*128*d + 2*128*d."""
+    centroid column with a non-zero count 2*128*d + 2*128*d.  Returns
+    (ops, exact tiles, centroid columns)."""
     exact_tiles = float((bmap == 1).sum())
     cen = (bmap == 2)
     # columns: per centroid block, the groups with count > 0
