@@ -1,24 +1,31 @@
-// Block-sparse INT8 attention forward (gfx950).
+// Block-sparse attention forward (gfx950): the INT8 path and the floating-QK
+// path, one kernel templated on the score type.
 //
 // Configure Sol Sparse Attention, "How it works": kept key blocks are computed
-// exactly on the INT8 Q/K (the W8A8 integer path), skipped blocks contribute
-// their centroids to the same online softmax (Configure H3 Static Virtual KV,
-// mode list, "residual").  FlashVSR Sparge Attention, "How it works": one sparse
-// call over the whole compact block map.
+// exactly on the INT8 Q/K (the W8A8 integer path) or, with a floating dense
+// backend, on the bf16 Q/K; skipped blocks contribute their centroids to the
+// same online softmax (Configure H3 Static Virtual KV, mode list, "residual").
+// FlashVSR Sparge Attention, "How it works": one sparse call over the whole
+// compact block map.
 //
 // Mapping onto CDNA4:
-//  * One workgroup (4 waves, 256 threads) per 128-row query block; wave w owns
-//    query rows 32w..32w+31.  Its INT8 Q fragment stays in registers for the
-//    whole kernel.
-//  * Exact 64-key tiles: K (int8) and V (bf16) are staged in LDS; S^T = K.Q^T
-//    with v_mfma_i32_32x32x32_i8 (two 32-key halves), so each lane ends up
-//    holding one query row's scores — the layout the PV product needs as its B
-//    operand, with no LDS round trip.  O^T = V^T.P^T with
-//    v_mfma_f32_32x32x16_bf16; the V^T operand comes straight from the
-//    row-major V tile through ds_read_b64_tr_b16.
+//  * One workgroup (4 waves, 256 threads) per 128-row query block, two per CU;
+//    wave w owns query rows 32w..32w+31.  Its Q fragment stays in registers
+//    for the whole kernel.
+//  * Exact 64-key tiles: K and V are copied straight into LDS (buffer loads
+//    into LDS, rows XOR-swizzled instead of padded); S^T = K.Q^T with
+//    v_mfma_i32_32x32x32_i8 (INT8) or v_mfma_f32_32x32x16_bf16 (bf16), so
+//    each lane ends up holding one query row's scores — the layout the PV
+//    product needs as its B operand, with no LDS round trip.
+//    O^T = V^T.P^T with v_mfma_f32_32x32x16_bf16; the V^T operand comes
+//    straight from the row-major V tile through ds_read_b64_tr_b16.
+//  * The tiles run as a software pipeline over 32-key halves: each step puts
+//    the next half's QK^T and the previous half's PV on the matrix cores and
+//    computes the current half's weights in their shadow (pipe_step).
 //  * Softmax in base 2 with sm_scale*log2(e) folded into the per-tile scale
-//    a_i*b_j; the running max is shared by the two lanes (l, l^32) that hold
-//    the same query row; row sums stay per lane until the end.
+//    (a_i*b_j on the INT8 path); the running max is shared by the two lanes
+//    (l, l^32) that hold the same query row and lags the scores while the
+//    weights stay small; row sums stay per lane until the end.
 //  * Centroid columns are batched 32 at a time into the same tile shapes, as
 //    bf16 hi+lo pairs (about 16 mantissa bits), with log2(count) added to the
 //    logit so a centroid weighs as much as the keys it stands for.
