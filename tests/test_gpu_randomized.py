@@ -49,7 +49,7 @@ def random_case(seed: int) -> W.Workload:
     return wl
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(576))
 def test_random_configuration(sa, orc, seed):
     wl = random_case(seed)
     _check_workload(orc, wl)
