@@ -364,3 +364,33 @@ def test_float_qk_and_topk_degenerate(sa, orc):
     wl.rule, wl.sparsity = 1, 0.99
     g, o = _check_workload(orc, wl)
     assert ((g["map"][..., :5] == 1).sum(-1) == 1).all()
+
+
+@pytest.mark.parametrize("rule,d,G,prefix", [(0, 128, 1, 0), (1, 128, 1, 1024), (0, 64, 2, 1024), (1, 64, 0, 0)])
+def test_long_rows(sa, orc, rule, d, G, prefix):
+    """Rows with more than 512 candidate key blocks (here up to 640) take the
+    decision kernels that recompute the proxies on every pass instead of
+    keeping a row's proxies in LDS: the threshold rule's mean and variance
+    over several passes, the fixed-sparsity rule's radix select."""
+    rng = np.random.default_rng(91 + d + 10 * rule)
+    H, Lq, Lkv = 2, 256, 640 * 64
+    lq_valid, lkv_valid = Lq - 5, Lkv - 40
+    q = W.iid_normal_bf16(rng, (1, H, Lq, d))
+    k = W.iid_normal_bf16(rng, (1, H, Lkv, d))
+    v = W.iid_normal_bf16(rng, (1, H, Lkv, d))
+    for t in (k, v):
+        t[0, :, lkv_valid:] = 0            # padding rows hold zeros
+    q[0, :, lq_valid:] = 0
+    wl = W.Workload("long_rows", 1, H, Lq, Lkv, d, lq_valid, lkv_valid, q, k, v, threshold=1.0,
+                    centroids_per_block=G, prefix_tokens=prefix, kblock=64, k_scale_rows=64)
+    wl.rule, wl.sparsity = rule, 0.7
+    g, o = _check_workload(orc, wl)
+    cand = (Lkv - prefix) // 64
+    assert cand > 512
+    nvalid = -(-lkv_valid // 64) - prefix // 64
+    routed = g["map"][..., prefix // 64:prefix // 64 + nvalid]
+    if rule == 1:   # the sparsity crosses the boundary as float32: 0.7f * 640 floors to 447
+        keep = nvalid - int(np.floor(float(np.float32(0.7)) * nvalid))
+        assert ((routed == EXACT).sum(-1) == keep).all()
+    else:
+        assert 0 < (routed == CENTROID).sum() < routed.size
