@@ -394,3 +394,21 @@ def test_long_rows(sa, orc, rule, d, G, prefix):
         assert ((routed == EXACT).sum(-1) == keep).all()
     else:
         assert 0 < (routed == CENTROID).sum() < routed.size
+
+
+@pytest.mark.parametrize("rule,G,prefix", [(0, 1, 0), (0, 2, 128), (1, 1, 0)])
+def test_batched(sa, orc, rule, G, prefix):
+    """B = 2: every kernel indexes (batch, head) pairs, the pooling kernels
+    through a batch grid dimension."""
+    rng = np.random.default_rng(95 + rule + 3 * G)
+    B, H, L, d, valid = 2, 3, 1024, 128, 1000
+    q = W.iid_normal_bf16(rng, (B, H, L, d))
+    k = W.iid_normal_bf16(rng, (B, H, L, d))
+    v = W.iid_normal_bf16(rng, (B, H, L, d))
+    for t in (q, k, v):
+        t[:, :, valid:] = 0
+    wl = W.Workload("batched", B, H, L, L, d, valid, valid, q, k, v, threshold=0.5, centroids_per_block=G,
+                    prefix_tokens=prefix, kblock=64, k_scale_rows=64)
+    wl.rule, wl.sparsity = rule, 0.5
+    g, o = _check_workload(orc, wl)
+    assert g["map"].shape[0] == B and not np.array_equal(g["map"][0], g["map"][1])
