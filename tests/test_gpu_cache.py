@@ -20,28 +20,28 @@ def sa():
     return m
 
 
-def _stream(seed, H, rows, d):
+def _stream(seed, H, rows, d, B=1):
     rng = np.random.default_rng(seed)
-    return bf16_bits(rng.standard_normal((1, H, rows, d)).astype(np.float32))
+    return bf16_bits(rng.standard_normal((B, H, rows, d)).astype(np.float32))
 
 
-@pytest.mark.parametrize("d,R", [(128, 128), (64, 64)])
-def test_cache_appends_bitexact(sa, orc, d, R):
+@pytest.mark.parametrize("d,R,B", [(128, 128, 1), (64, 64, 1), (128, 128, 2)])
+def test_cache_appends_bitexact(sa, orc, d, R, B):
     """Chunks with wrap-around and a partial last slab, against the oracle's
     ring after the same appends."""
     H, slots = 3, 6
     chunks = [(3, None), (2, None), (4, None), (2, R + 40)]   # (slabs, valid rows)
     total = sum(n for n, _ in chunks)
-    x = _stream(41, H, total * R, d)
-    gq = torch.zeros((1, H, slots * R, d), dtype=torch.int8, device="cuda")
-    gs = torch.zeros((1, H, slots), dtype=torch.float32, device="cuda")
-    oq = np.zeros((1, H, slots * R, d), np.int8)
-    osc = np.zeros((1, H, slots), np.float32)
+    x = _stream(41, H, total * R, d, B)
+    gq = torch.zeros((B, H, slots * R, d), dtype=torch.int8, device="cuda")
+    gs = torch.zeros((B, H, slots), dtype=torch.float32, device="cuda")
+    oq = np.zeros((B, H, slots * R, d), np.int8)
+    osc = np.zeros((B, H, slots), np.float32)
     g = 0
     slot = 0
     for n, valid in chunks:
         part = x[:, :, g * R:(g + n) * R]
-        say(f"case cache append d={d} R={R} slabs={n} first_slot={slot} valid={valid}")
+        say(f"case cache append B={B} d={d} R={R} slabs={n} first_slot={slot} valid={valid}")
         nxt = sa.kv_cache_append_int8(bf16_dev(part), gq, gs, slot, valid_len=valid, rows_per_slab=R)
         orc.cache_append(oq, osc, part, first_slot=slot, valid_len=valid, rows_per_slab=R)
         assert nxt == (slot + n) % slots

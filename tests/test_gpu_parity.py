@@ -118,6 +118,20 @@ def test_gather_bitexact(sa, orc):
     assert np.array_equal(g8.cpu().numpy(), kq.cpu().numpy()) and np.array_equal(gs.cpu().numpy(), ks.cpu().numpy())
 
 
+def test_gather_batched(sa, orc):
+    """Two batch entries of physical K through the same source map."""
+    wl = W.config(5, small=True)
+    rng = np.random.default_rng(97)
+    k2 = np.concatenate([wl.k, W.iid_normal_bf16(rng, wl.k.shape)], axis=0)
+    say(f"case gather batched B={k2.shape[0]}")
+    kq, ks, vbs = sa.gather_virtual_kv(bf16_dev(k2), wl.rows_per_slice, wl.src_map.tolist(),
+                                       torch.from_numpy(wl.rope_cos).cuda(), torch.from_numpy(wl.rope_sin).cuda())
+    o8, os_, ovbs = orc.gather_virtual_kv(k2, wl.rows_per_slice, wl.src_map, wl.rope_cos, wl.rope_sin)
+    assert kq.shape[0] == 2
+    assert np.array_equal(kq.cpu().numpy(), o8) and np.array_equal(ks.cpu().numpy(), os_)
+    assert np.array_equal(vbs.cpu().numpy(), ovbs)
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_workload_small(sa, orc, n):
     _check_workload(orc, W.config(n, small=True))
