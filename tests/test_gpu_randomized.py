@@ -11,7 +11,8 @@ from tests.test_gpu_parity import _check_workload, sa  # noqa: F401  (fixture)
 pytestmark = pytest.mark.gpu
 
 
-def random_case(seed: int) -> W.Workload:
+def random_case(seed: int, max_blocks: int = 5) -> W.Workload:
+    """Segments of up to max_blocks key blocks each (1-4 of them)."""
     rng = np.random.default_rng(1000 + seed)
     d = int(rng.choice([64, 128]))
     kblock = int(rng.choice([64, 128]))
@@ -22,7 +23,7 @@ def random_case(seed: int) -> W.Workload:
     # key layout: 1-4 segments on key-block boundaries with random padding
     segs, cursor = [], 0
     for _ in range(int(rng.integers(1, 5))):
-        rows = int(rng.integers(1, 5 * kblock))
+        rows = int(rng.integers(1, max_blocks * kblock))
         segs.append((cursor, rows, int(rng.integers(0, 2))))
         cursor += -(-rows // kblock) * kblock + kblock * int(rng.integers(0, 2))
     if not any(r for _, _, r in segs):
@@ -52,4 +53,12 @@ def random_case(seed: int) -> W.Workload:
 @pytest.mark.parametrize("seed", range(576))
 def test_random_configuration(sa, orc, seed):
     wl = random_case(seed)
+    _check_workload(orc, wl)
+
+
+@pytest.mark.parametrize("seed", range(2000, 2064))
+def test_random_configuration_medium(sa, orc, seed):
+    """Segments of up to 12 key blocks (up to ~6K keys): several rounds
+    of workgroups, longer tile lists and their ragged ends."""
+    wl = random_case(seed, max_blocks=12)
     _check_workload(orc, wl)
