@@ -108,7 +108,11 @@ void orc_quantize(const uint16_t* x, int64_t sB, int64_t sH, int64_t sL, int B, 
 /* Dequantized value of V at logical row r, channel c (bf16 or INT8 cache).
  * With a block source table, logical 64-row block r/64 reads physical block
  * v_block_src[r/64] (Configure H3 Static Virtual KV, mode list: V is never
- * copied, only re-read). */
+ * copied, only re-read); an INT8 V takes the scale of the physical row.
+ * Pinned by: route and forward through the table equal SDPA and numpy means on
+ * a V materialized by concatenating the physical slices in source-map order,
+ * and, for INT8 V with 64- and 128-row physical scales, the results on a
+ * materialized INT8 V. */
 typedef struct {
   const uint16_t* v_bf16;
   const int8_t* v_i8;
@@ -444,7 +448,9 @@ int orc_route(const int8_t* q, const int8_t* k, const float* k_scale, int k_scal
 /* float64), LCSA map == masked dense attention, single-block centroid       */
 /* closed forms, identical-key blocks (centroid == exact, count weighting);  */
 /* the floating path: all-exact == SDPA on the bf16 inputs, a single        */
-/* centroid block gives vbar.                                                 */
+/* centroid block gives vbar, and a mix of exact keys and 2x32 centroid      */
+/* columns equals a softmax over explicitly listed columns (bf16 query      */
+/* against kbar, 1/sqrt(d), ln(count) bias).                                  */
 /* ------------------------------------------------------------------------- */
 void orc_forward(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale,
                  int k_scale_rows, const uint16_t* v_bf16, const int8_t* v_i8, const float* v_scale,

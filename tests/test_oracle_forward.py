@@ -231,3 +231,42 @@ def test_float_path_single_centroid_block_outputs_vbar(orc):
                             count=r["count"], v_bits=v, G=1, q_bits=q, k_bits=k)
     vbar = bf16_to_f32(v)[0, 0, :n].astype(np.float64).mean(0)
     assert np.abs(out.reshape(Lq, -1) - vbar[None]).max() < 1e-14
+
+
+def test_float_path_centroid_mix_matches_explicit_logit_softmax(orc):
+    """Floating QK path with exact keys and several 2x32 centroid columns per
+    row, against a float64 torch.softmax over explicitly listed columns: exact
+    keys with logit q.k / sqrt(d) on the bf16 values, centroid columns with
+    logit q.kbar / sqrt(d) + ln(count) on the bf16 query, kbar the mean of the
+    dequantized INT8 keys of the group (the centroids are routed on the codes
+    whatever the backend).  Several centroid columns with different logits per
+    row make the logit's scale and its query operand matter."""
+    wl = W.tiny_sol(seed=37, H=1, L=512, d=64, valid=500)
+    q8, qs = orc.quantize(wl.q, 500, 128)
+    k8, ks = orc.quantize(wl.k, 500, 64)
+    r = orc.route(q8, k8, ks, 64, 500, 500, v_bits=wl.v, tau=-0.3, G=2)
+    cen = (r["map"] == CENTROID).sum(-1)
+    assert cen.min() >= 2 and (r["map"] == EXACT).sum(-1).min() >= 2
+    out, lse, _ = orc.forward(q8, qs, k8, ks, 64, 500, 500, r["map"], kbar=r["kbar"], vbar=r["vbar"],
+                              count=r["count"], v_bits=wl.v, G=2, q_bits=wl.q, k_bits=wl.k)
+    qf, kf, vf = (bf16_to_f32(t)[0, 0].astype(np.float64) for t in (wl.q, wl.k, wl.v))
+    kd = _deq(k8, ks, 64)[0, 0]
+    for i in range(4):
+        cols_k, cols_v, bias = [], [], []
+        for j in range(8):
+            rows = [u for u in range(j * 64, j * 64 + 64) if u < 500]
+            if r["map"][0, 0, i, j] == EXACT:
+                cols_k += [kf[u] for u in rows]; cols_v += [vf[u] for u in rows]; bias += [0.0] * len(rows)
+            elif r["map"][0, 0, i, j] == CENTROID:
+                for g in range(2):
+                    grp = [u for u in rows if j * 64 + g * 32 <= u < j * 64 + g * 32 + 32]
+                    if not grp:
+                        continue
+                    cols_k.append(kd[grp].mean(0)); cols_v.append(vf[grp].mean(0)); bias.append(math.log(len(grp)))
+        r1 = min(128, 500 - i * 128)
+        logit = qf[i * 128:i * 128 + r1] @ np.array(cols_k).T / 8.0 + np.array(bias)
+        p = torch.softmax(torch.from_numpy(logit), dim=-1).numpy()
+        ref = p @ np.array(cols_v)
+        assert np.abs(out[i, :r1] - ref).max() < 1e-12
+        ref_lse = torch.logsumexp(torch.from_numpy(logit), dim=-1).numpy()
+        assert np.abs(lse[i, :r1] - ref_lse).max() < 1e-10
