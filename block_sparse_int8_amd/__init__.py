@@ -131,6 +131,22 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _keep_for(stream, *tensors):
+    """Tensors allocated here (on torch's current stream) that kernels queued on
+    another ``stream`` use: record that stream on them, so the caching
+    allocator does not hand their memory out again before those kernels are
+    done, even when the Python objects are released first."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+        stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, contiguous=True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -164,6 +180,7 @@ def quantize_qk_int8(x: torch.Tensor, valid_len: Optional[int] = None, rows_per_
     _need(scale, "scale", torch.float32, (B, H, L // rows_per_block))
     _check(load().quantize_qk_int8(_ptr(x), x.stride(0), x.stride(1), x.stride(2), B, H, L, d, valid_len,
                                    rows_per_block, _ptr(out), _ptr(scale), _stream(stream)))
+    _keep_for(stream, out, scale)
     return out, scale
 
 
@@ -258,7 +275,11 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
             kc = torch.empty((B, H, nKB, G, d), dtype=torch.float32, device=dev)
             vc = torch.empty((B, H, nKB, G, d), dtype=torch.float32, device=dev)
             cnt = torch.empty((B, H, nKB, G), dtype=torch.float32, device=dev)
-    stats = torch.empty((B, H, nQB, 2), dtype=torch.float64, device=dev) if row_stats else None
+    stats = outputs.get("row_stats")
+    if stats is None and row_stats:
+        stats = torch.empty((B, H, nQB, 2), dtype=torch.float64, device=dev)
+    if stats is not None:
+        _need(stats, "row_stats", torch.float64, (B, H, nQB, 2))
     ws_bytes = lib.sparse_attn_route_workspace_size(ctypes.byref(dims), ctypes.byref(prm),
                                                     1 if explicit_map is not None else 0)
     if workspace is None and ws_bytes:
@@ -273,6 +294,7 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
                                  _ptr(v_block_src), ctypes.byref(dims), ctypes.byref(prm), _ptr(explicit_map),
                                  _ptr(bmap), _ptr(kc), _ptr(vc), _ptr(cnt), _ptr(stats), ws_ptr, ws_avail,
                                  _stream(stream)))
+    _keep_for(stream, bmap, kc, vc, cnt, stats, workspace)
     return dict(map=bmap, k_centroid=kc, v_centroid=vc, count=cnt, row_stats=stats, workspace=workspace)
 
 
@@ -325,6 +347,7 @@ def sparse_attn_fwd(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k
                                   _ptr(v_block_src), ctypes.byref(dims), ctypes.byref(prm), _ptr(block_map),
                                   _ptr(k_centroid), _ptr(v_centroid), _ptr(count), float(sm), _ptr(out), odt,
                                   _ptr(lse), _stream(stream)))
+    _keep_for(stream, out, lse)
     return (out, lse) if return_lse else out
 
 
@@ -367,6 +390,7 @@ def sparse_attn_fwd_float(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blo
     _check(load().sparse_attn_fwd_float(_ptr(q), _ptr(k), _ptr(v), _ptr(v_block_src), ctypes.byref(dims),
                                         ctypes.byref(prm), _ptr(block_map), _ptr(k_centroid), _ptr(v_centroid),
                                         _ptr(count), float(sm), _ptr(out), odt, _ptr(lse), _stream(stream)))
+    _keep_for(stream, out, lse)
     return (out, lse) if return_lse else out
 
 
@@ -390,6 +414,7 @@ def gather_virtual_kv(k_phys: torch.Tensor, rows_per_slice: int, src_map: Sequen
     _check(load().gather_virtual_kv(_ptr(k_phys), B, H, S, Lp // S if S else 0, d, src, n_logical, _ptr(rope_cos),
                                     _ptr(rope_sin), rot_offset, d_rot, k_rows_per_block, _ptr(kq), _ptr(ks),
                                     _ptr(vbs), _stream(stream)))
+    _keep_for(stream, kq, ks, vbs)
     return kq, ks, vbs
 
 

@@ -182,9 +182,12 @@ __device__ __forceinline__ void load_v_int8(const int8_t* vsrc, VRegs<D>& vr, in
   }
 }
 
+// The LDS addresses are formed from the thread index at each call (opaque to
+// the compiler): kept live across the tile loop instead, they would be spilled.
 template <int D>
 __device__ __forceinline__ void store_v_int8(uint8_t* vbuf, const VRegs<D>& vr, int tid) {
   using L = FwdLds<D>;
+  tid = opaque(tid);
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) {
     const int v = tid + 256 * e, r = v / (D / 16), cc = v % (D / 16);
@@ -814,6 +817,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       tile_copy<D, KB, VI8>(t, t, kst0, vst0, krs, vrs, plan, wave).all();
       if (VI8) store_v_int8<D>(vst0, vr, tid);
       copies_done_barrier();
+      // Keys at or past nvalid get weight 0, but their V rows are padding and
+      // may hold anything (NaN, Inf): clear them so that 0 * V stays 0 in the
+      // PV product.
+      for (int u = tid; u < (kTile - nvalid) * (L::VROW / 16); u += 256) {
+        const int r = nvalid + u / (L::VROW / 16), x = (u % (L::VROW / 16)) * 16;
+        *reinterpret_cast<v4i*>(vst0 + L::v_off(r, x)) = (v4i){0, 0, 0, 0};
+      }
+      __syncthreads();
       masked_tile<D, QF, VI8>(kst0, vst0, qf, seed, O, m_run, l_run, qc * t.kscale, t.pscale, nvalid, lo, hh);
       __syncthreads();
     }
@@ -928,29 +939,36 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 
   // ---------------- finalize ----------------
+  // Padded rows and rows with nothing to attend are written as 0 by a select
+  // (not by a zero factor, which would keep a NaN from a padded query row).
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const bool row_ok = qrow < a.lq_valid && l_tot > 0.0f;
+  // the output row, formed again from the thread index (kept live across the
+  // tile loop instead, it would be spilled)
+  const int qrow_out = i * kQBlock + ((opaque(tid) >> 6) << 5) + n;   // wave * 32 + n
+  const bool row_ok = qrow_out < a.lq_valid && l_tot > 0.0f;
   const float inv = row_ok ? 1.0f / l_tot : 0.0f;
 #pragma unroll
   for (int cb = 0; cb < NS; ++cb) {
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const int ch = cb * 32 + gq * 8 + hh * 4;
-      const int64_t o = (bh * a.Lq + qrow) * D + ch;
+      const int64_t o = (bh * a.Lq + qrow_out) * D + ch;
       if (OBF16) {
         v4bf r;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) r[e2] = (__bf16)(O[cb][gq * 4 + e2] * inv);
+        for (int e2 = 0; e2 < 4; ++e2) r[e2] = (__bf16)(row_ok ? O[cb][gq * 4 + e2] * inv : 0.0f);
         *reinterpret_cast<v4bf*>(static_cast<uint16_t*>(a.out) + o) = r;
       } else {
-        float4 r = make_float4(O[cb][gq * 4] * inv, O[cb][gq * 4 + 1] * inv, O[cb][gq * 4 + 2] * inv,
-                               O[cb][gq * 4 + 3] * inv);
+        float x[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) x[e2] = row_ok ? O[cb][gq * 4 + e2] * inv : 0.0f;
+        const float4 r = make_float4(x[0], x[1], x[2], x[3]);
         *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = r;
       }
     }
   }
   if (a.lse && hh == 0)
-    a.lse[bh * a.Lq + qrow] = row_ok ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    a.lse[bh * a.Lq + qrow_out] = row_ok ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
 }
 
 template <int D, bool VI8>

@@ -218,8 +218,10 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
 // D_ij = Qsum_i . Ksum_j is exact: with x = 128*hi + lo for both sums,
 //   D = 2^14 * sum(hq*hk) + 2^7 * sum(hq*lk + lq*hk) + sum(lq*lk),
 // three v_mfma_i32_32x32x32_i8 products (the middle one over 2d), each partial
-// sum below 2^22 in int32, combined exactly in float64.  s_ij = D * (b_j / n_j)
-// in float64.  A 32x32 tile costs 16 MFMAs, so the decision kernels recompute
+// sum below 2^22 in int32, combined exactly in float64.  s_ij = (D * b_j) / n_j
+// in float64, rounded after the product and after the quotient, so it is the
+// same float64 value whatever evaluates it in that order.  A 32x32 tile costs
+// 16 MFMAs, so the decision kernels recompute
 // s on every pass over the key blocks instead of storing it.
 //
 // Lane (n, hf) of a tile holds s[r][j] for rows r = (e/4)*8 + hf*4 + e%4
@@ -266,10 +268,12 @@ struct ProxyTiles {
       p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ql[s], k.l[s], p3, 0, 0, 0);
     }
     const int nj = j < a.nKB ? a.lay.block_rows(j) : 0;
-    const double w = nj > 0 ? (double)a.k_scale[bh * nKS + j] / (double)nj : 0.0;
+    const double bj = nj > 0 ? (double)a.k_scale[bh * nKS + j] : 0.0, nd = nj > 0 ? (double)nj : 1.0;
+    // D is an exact integer in float64; then one rounding for the product
+    // and one for the quotient, in that order
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-      sv[e] = (16384.0 * (double)p1[e] + 128.0 * (double)p2[e] + (double)p3[e]) * w;
+      sv[e] = ((16384.0 * (double)p1[e] + 128.0 * (double)p2[e] + (double)p3[e]) * bj) / nd;
   }
   __device__ __forceinline__ int row_of(int e) const { return (e / 4) * 8 + hf * 4 + (e % 4); }
 };

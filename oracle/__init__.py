@@ -235,7 +235,8 @@ def run(wl, sel=None, tau=None):
         k8, ks = quantize(wl.k, wl.lkv_valid, wl.k_scale_rows)
     vkw = {}
     if wl.v_int8:
-        v8, vs = quantize(wl.v, wl.lkv_valid, wl.v_scale_rows)
+        # a virtual context's V is its physical slices, all valid
+        v8, vs = quantize(wl.v, wl.v.shape[2] if wl.virtual else wl.lkv_valid, wl.v_scale_rows)
         vkw = dict(v8=v8, v_scale=vs, v_scale_rows=wl.v_scale_rows)
     else:
         vkw = dict(v_bits=wl.v)

@@ -48,7 +48,8 @@ def gpu_pipeline(wl, tau=None, out_dtype=torch.float32, kblock=None, map_kblock=
         k8, ks = sa.quantize_qk_int8(k, wl.lkv_valid, wl.k_scale_rows)
     v_in, vsc = v, None
     if wl.v_int8:
-        v_in, vsc = sa.quantize_qk_int8(v, wl.lkv_valid, wl.v_scale_rows)
+        # a virtual context's V is its physical slices, all valid
+        v_in, vsc = sa.quantize_qk_int8(v, wl.v.shape[2] if wl.virtual else wl.lkv_valid, wl.v_scale_rows)
     em = None
     if wl.explicit_map is not None:
         em = torch.from_numpy(np.ascontiguousarray(wl.explicit_map)).cuda()

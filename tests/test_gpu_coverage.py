@@ -1,0 +1,225 @@
+"""GPU parity for the INT8-V cache with centroids, padding that holds
+non-finite values, guard bands around every output, and the routing
+statistics.
+
+FlashVSR Kitchen Sparse Attention, opening section: K/V arrive as an INT8
+cache with one scale per 128-row slab; Configure Sol Sparse Attention, "How it
+works": skipped blocks still contribute their centroids, here built from that
+INT8 V.  Padding rows (past the valid length, or between segments) take no part
+in the softmax, whatever they hold.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from workloads import CENTROID, DROP, EXACT, bf16_bits
+from tests.helpers import MAX_ABS, MEAN_ABS, bf16_dev, compare_maps, gpu_pipeline, say
+from tests.test_gpu_parity import _check_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sa():
+    import block_sparse_int8_amd as m
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    m.device_check(torch.cuda.current_device())
+    return m
+
+
+# ---------------------------------------------------------------------------
+# INT8 V with centroids
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,G,kblock,vrows", [(128, 1, 64, 128), (128, 2, 64, 64), (64, 1, 64, 128),
+                                              (64, 2, 128, 128), (128, 2, 128, 64)])
+def test_int8_v_sol_rule_with_centroids(sa, orc, d, G, kblock, vrows):
+    """The Sol rule over an INT8 V cache: V-bar dequantized through the V scales,
+    the INT8-V forward with centroid columns (d = 64 and 128)."""
+    wl = W.tiny_sol(seed=70 + d + G + kblock, H=2, L=1024, d=d, valid=1000, centroids_per_block=G)
+    wl.kblock = wl.k_scale_rows = kblock
+    wl.v_int8, wl.v_scale_rows = True, vrows
+    g, o = _check_workload(orc, wl, tau=0.5)
+    assert (g["map"] == CENTROID).any() and (g["map"] == EXACT).any()
+
+
+@pytest.mark.parametrize("d,G,kblock,ksr", [(128, 1, 128, 64), (128, 2, 128, 64), (64, 2, 128, 128),
+                                            (128, 2, 64, 64), (64, 1, 64, 64)])
+def test_int8_v_explicit_centroid_map(sa, orc, d, G, kblock, ksr):
+    """Explicit maps with EXACT / CENTROID / DROP entries over an INT8 K/V cache,
+    including 128-key blocks whose K carries one scale per 64 rows (a centroid
+    group then combines two scale blocks)."""
+    L, H = 1024, 2
+    wl = W.tiny_sol(seed=80 + d + G, H=H, L=L, d=d, valid=1000, centroids_per_block=G)
+    wl.kblock, wl.k_scale_rows, wl.map_kblock = kblock, ksr, kblock
+    wl.v_int8, wl.v_scale_rows = True, 128
+    rng = np.random.default_rng(81 + kblock)
+    wl.explicit_map = rng.choice(np.array([EXACT, CENTROID, DROP], np.uint8), size=(1, H, L // 128, L // kblock),
+                                 p=[0.45, 0.45, 0.1])
+    g, o = _check_workload(orc, wl)
+    assert (g["map"] == CENTROID).sum() > 0
+
+
+def test_int8_v_virtual_table_with_centroids(sa, orc):
+    """INT8 V read through the virtual-KV block table (64-row logical blocks
+    from physical blocks) with 2x32 centroids: V-bar and the exact tiles both
+    read the remapped rows and their scales."""
+    wl = W.config(5, small=True)
+    wl.v_int8, wl.v_scale_rows = True, 128
+    _check_workload(orc, wl)
+
+
+# ---------------------------------------------------------------------------
+# Padding holding non-finite values
+# ---------------------------------------------------------------------------
+
+def _poison(bits, rows, values):
+    """Copy of bf16 bits with the given rows (indices along L) cycling through values."""
+    out = bits.copy()
+    pat = bf16_bits(np.array(values, np.float32))
+    for n, r in enumerate(rows):
+        out[:, :, r, :] = pat[(n + np.arange(bits.shape[3])) % len(pat)]
+    return out
+
+
+@pytest.mark.parametrize("qk_float", [False, True])
+def test_nonfinite_padding_is_ignored(sa, qk_float):
+    """V rows past the valid length and inside segment padding, and (floating
+    path) Q and K rows past the valid length, filled with NaN and +-Inf: the
+    outputs, lse, map and centroids equal those of the zero-padded run bit for
+    bit.  (K rows inside the layout's padding stay zero: the quantizer does not
+    know the layout, and the header asks for zeros there.)"""
+    wl = W.ref2va_segments(H=2, text=77, ref_image=300, ref_audio=40, ref_video_frames=1, video_frames=2,
+                           frame_tokens=320, centroids_per_block=2)
+    wl.qk_float = qk_float
+    ref = gpu_pipeline(wl)
+    pad_rows = []
+    segs = wl.segments
+    for x in range(len(segs)):
+        end = int(segs[x][0] + segs[x][1])
+        nxt = int(segs[x + 1][0]) if x + 1 < len(segs) else wl.Lkv
+        pad_rows += list(range(end, nxt))
+    assert len(pad_rows) > 64
+    vals = [np.nan, np.inf, -np.inf, 3.0e38]
+    bad = W.Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
+    bad.v = _poison(wl.v, pad_rows, vals)
+    tail = list(range(wl.lkv_valid, wl.Lkv))
+    if qk_float:
+        bad.q = _poison(wl.q, list(range(wl.lq_valid, wl.Lq)), vals)
+        bad.k = _poison(wl.k, tail, vals)
+    say(f"case nonfinite padding qk_float={qk_float}: {len(pad_rows)} V rows, {len(tail)} tail rows")
+    got = gpu_pipeline(bad)
+    for key in ("map", "kbar", "vbar", "count", "out", "lse"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert np.isfinite(got["out"]).all()
+
+
+# ---------------------------------------------------------------------------
+# Guard bands around the outputs
+# ---------------------------------------------------------------------------
+
+GUARD = 4096
+FILL = 0xA5
+
+
+def _guarded(shape, dtype):
+    """A tensor of `shape` inside a byte buffer with GUARD bytes of FILL on each
+    side; returns (tensor, buffer)."""
+    nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    buf = torch.full((nbytes + 2 * GUARD,), FILL, dtype=torch.uint8, device="cuda")
+    t = buf[GUARD:GUARD + nbytes].view(dtype).view(shape)
+    return t, buf
+
+
+def _guards_intact(buf):
+    h = buf.cpu().numpy()
+    return bool((h[:GUARD] == FILL).all() and (h[-GUARD:] == FILL).all())
+
+
+@pytest.mark.parametrize("case", ["tiny_sol", "segments_2x32", "segments_topk", "float_qk"])
+def test_guard_bands_untouched(sa, orc, case):
+    """Quantized Q/K, scales, map, centroids, counts, row statistics, output
+    and lse are written into buffers with guard bands of a known byte on both
+    sides; after quantize, route and forward the guards are unchanged and the
+    results still match the oracle."""
+    if case == "tiny_sol":
+        wl = W.config(1)
+    else:
+        wl = W.ref2va_segments(H=2, text=77, ref_image=300, ref_audio=40, ref_video_frames=1, video_frames=2,
+                               frame_tokens=320, centroids_per_block=2)
+        if case == "segments_topk":
+            wl.rule, wl.sparsity = 1, 0.75
+        if case == "float_qk":
+            wl.qk_float = True
+    say(f"case guards {case}")
+    B, H, Lq, d = wl.q.shape
+    Lkv, G, kb = wl.Lkv, wl.centroids_per_block, wl.kblock
+    nQB, nKB = Lq // 128, Lkv // kb
+    bufs = []
+
+    def g(shape, dtype):
+        t, b = _guarded(shape, dtype)
+        bufs.append(b)
+        return t
+
+    q, k, v = bf16_dev(wl.q), bf16_dev(wl.k), bf16_dev(wl.v)
+    q8, qs = sa.quantize_qk_int8(q, wl.lq_valid, 128, out=g((B, H, Lq, d), torch.int8),
+                                 scale=g((B, H, nQB), torch.float32))
+    k8, ks = sa.quantize_qk_int8(k, wl.lkv_valid, kb, out=g((B, H, Lkv, d), torch.int8),
+                                 scale=g((B, H, Lkv // kb), torch.float32))
+    outs = dict(map=g((B, H, nQB, nKB), torch.uint8), k_centroid=g((B, H, nKB, G, d), torch.float32),
+                v_centroid=g((B, H, nKB, G, d), torch.float32), count=g((B, H, nKB, G), torch.float32),
+                row_stats=g((B, H, nQB, 2), torch.float64))
+    r = sa.sparse_attn_route(q8, k8, ks, v, lq_valid=wl.lq_valid, lkv_valid=wl.lkv_valid, threshold=wl.threshold,
+                             centroids_per_block=G, kblock=kb, rule=wl.rule, sparsity=wl.sparsity,
+                             segments=wl.segments, outputs=outs, row_stats=True)
+    out, lse = g((B, H, Lq, d), torch.float32), g((B, H, Lq), torch.float32)
+    kw = dict(k_centroid=r["k_centroid"], v_centroid=r["v_centroid"], count=r["count"], lq_valid=wl.lq_valid,
+              lkv_valid=wl.lkv_valid, centroids_per_block=G, kblock=kb, sm_scale=wl.sm_scale, out=out, lse=lse,
+              return_lse=True, segments=wl.segments)
+    if wl.qk_float:
+        sa.sparse_attn_fwd_float(q, k, v, r["map"], **kw)
+    else:
+        sa.sparse_attn_fwd(q8, qs, k8, ks, v, r["map"], **kw)
+    torch.cuda.synchronize()
+    for n, b in enumerate(bufs):
+        assert _guards_intact(b), f"guard band of buffer {n} was written"
+    assert r["row_stats"].data_ptr() == outs["row_stats"].data_ptr()
+    o = orc.run(wl)
+    bad, _, _ = compare_maps(r["map"].cpu().numpy(), o["map"], o["tie"])
+    assert bad == 0
+    diff = np.abs(out.cpu().numpy().reshape(B * H, Lq, d) - o["out"].reshape(B * H, Lq, d))[:, :wl.lq_valid]
+    assert diff.max() <= MAX_ABS and diff.mean() <= MEAN_ABS
+
+
+# ---------------------------------------------------------------------------
+# Routing statistics and proxies at partial blocks
+# ---------------------------------------------------------------------------
+
+def test_row_stats_and_partial_block_proxies(sa, orc):
+    """The threshold rule's per-row mean and population std against the
+    oracle's float64 values (the only difference is the summation order, a few
+    ulps), on a layout with partial key blocks at every segment end; and the
+    fixed-sparsity rule on the same layout bit-exact with no tie band, which
+    holds only if the proxies of partial blocks (n < 64) are the oracle's
+    float64 values bit for bit."""
+    wl = W.ref2va_segments(H=3, text=77, ref_image=300, ref_audio=40, ref_video_frames=1, video_frames=3,
+                           frame_tokens=333, centroids_per_block=1)
+    ends = [int(s[0] + s[1]) for s in wl.segments]
+    assert any(e % 64 for e in ends)
+    g = gpu_pipeline(wl)
+    o = orc.run(wl)
+    st = np.isfinite(o["stats"])
+    assert st.all()
+    # mu and sigma of a row within 1e-12 of |mu| + sigma (the tie band is 1e-6 sigma)
+    mu, sig = o["stats"][..., 0], o["stats"][..., 1]
+    scale = (np.abs(mu) + sig)[..., None]
+    err = np.abs(g["stats"] - o["stats"]) / scale
+    assert err.max() < 1e-12, err.max()
+    for sp in (0.3, 0.5, 0.75, 0.9):
+        wl.rule, wl.sparsity = 1, sp
+        g = gpu_pipeline(wl)
+        o = orc.run(wl)
+        assert np.array_equal(g["map"], o["map"]), sp
