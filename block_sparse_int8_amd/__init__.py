@@ -23,7 +23,7 @@ from typing import Optional, Sequence
 
 import torch
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 SA_OK, SA_E_NULL, SA_E_SHAPE, SA_E_ALIGN, SA_E_VALUE, SA_E_UNSUPPORTED, SA_E_DEVICE, SA_E_LAUNCH, SA_E_WORKSPACE = range(9)
 SA_DROP, SA_EXACT, SA_CENTROID = 0, 1, 2
 SA_BF16, SA_INT8, SA_F32 = 0, 1, 2
@@ -93,6 +93,9 @@ def load(path: Optional[str] = None):
     lib.sparse_attn_route.argtypes = [vp, vp, vp, vp, i32, vp, vp, P(sa_dims), P(sa_route_params), vp, vp, vp, vp,
                                       vp, vp, vp, ctypes.c_size_t, vp]
     lib.sparse_attn_route.restype = i32
+    lib.sparse_attn_route_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, vp, P(sa_dims), P(sa_route_params), vp, vp,
+                                              vp, vp, vp, vp, vp]
+    lib.sparse_attn_route_noalloc.restype = i32
     lib.sparse_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, P(sa_dims), P(sa_route_params), vp, vp, vp, vp,
                                     f32, vp, i32, vp, vp]
     lib.sparse_attn_fwd.restype = i32
@@ -231,12 +234,14 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
                       explicit_map: Optional[torch.Tensor] = None, map_kblock: Optional[int] = None,
                       rule: int = SA_RULE_THRESHOLD, sparsity: float = 0.0, segments=None,
                       row_stats: bool = False, workspace: Optional[torch.Tensor] = None,
-                      outputs: Optional[dict] = None, stream=None) -> dict:
+                      outputs: Optional[dict] = None, noalloc: bool = False, stream=None) -> dict:
     """Block map + centroids.  ``rule`` picks the threshold rule (``threshold``)
     or the fixed-sparsity rule (``sparsity``); ``segments`` ((start, rows,
     routed) triples) gives a segmented key layout in place of the prefix.
     Returns dict(map, k_centroid, v_centroid, count, row_stats) with the shapes
-    of sparse_attn.h."""
+    of sparse_attn.h.  ``noalloc`` calls sparse_attn_route_noalloc (library-owned
+    workspace; pass every output in ``outputs`` for a call that allocates
+    nothing)."""
     B, H, Lq, d = q8.shape
     Lkv = k8.shape[2]
     Lv = v.shape[2]
@@ -280,6 +285,13 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
         stats = torch.empty((B, H, nQB, 2), dtype=torch.float64, device=dev)
     if stats is not None:
         _need(stats, "row_stats", torch.float64, (B, H, nQB, 2))
+    if noalloc:
+        _check(lib.sparse_attn_route_noalloc(_ptr(q8), _ptr(k8), _ptr(k_scale), _ptr(v), v_dtype, _ptr(v_scale),
+                                             _ptr(v_block_src), ctypes.byref(dims), ctypes.byref(prm),
+                                             _ptr(explicit_map), _ptr(bmap), _ptr(kc), _ptr(vc), _ptr(cnt),
+                                             _ptr(stats), _stream(stream)))
+        _keep_for(stream, bmap, kc, vc, cnt, stats)
+        return dict(map=bmap, k_centroid=kc, v_centroid=vc, count=cnt, row_stats=stats, workspace=None)
     ws_bytes = lib.sparse_attn_route_workspace_size(ctypes.byref(dims), ctypes.byref(prm),
                                                     1 if explicit_map is not None else 0)
     if workspace is None and ws_bytes:
@@ -296,6 +308,14 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
                                  _stream(stream)))
     _keep_for(stream, bmap, kc, vc, cnt, stats, workspace)
     return dict(map=bmap, k_centroid=kc, v_centroid=vc, count=cnt, row_stats=stats, workspace=workspace)
+
+
+def sparse_attn_route_noalloc(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor, v: torch.Tensor,
+                              **kw) -> dict:
+    """sparse_attn_route on the library-owned workspace (no ``workspace``
+    argument); see sparse_attn_route for the keywords."""
+    kw.pop("workspace", None)
+    return sparse_attn_route(q8, k8, k_scale, v, noalloc=True, **kw)
 
 
 def sparse_attn_fwd(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,

@@ -61,12 +61,13 @@ int32_t check_device(int dev) {
   return SA_OK;
 }
 
-int32_t check_current_device() {
+int32_t check_current_device(int* dev_out = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return fail(SA_E_DEVICE, "no current HIP device");
   }
+  if (dev_out) *dev_out = dev;
   return check_device(dev);
 }
 
@@ -224,11 +225,18 @@ size_t sparse_attn_route_workspace_size(const sa_dims* dims, const sa_route_para
   return sa::route_workspace_bytes(dims->B, dims->H, dims->Lq / 128, dims->Lkv / p->kblock, dims->d);
 }
 
-int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale, const void* v, int32_t v_dtype,
-                          const float* v_scale, const int32_t* v_block_src, const sa_dims* dims,
-                          const sa_route_params* p, const uint8_t* explicit_map, uint8_t* block_map,
-                          float* k_centroid, float* v_centroid, float* count, double* row_stats, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The routing pass behind sparse_attn_route (workspace from the caller) and
+// sparse_attn_route_noalloc (library-owned workspace: `noalloc` set, and
+// workspace / workspace_bytes ignored).
+int32_t route_impl(const int8_t* q, const int8_t* k, const float* k_scale, const void* v, int32_t v_dtype,
+                   const float* v_scale, const int32_t* v_block_src, const sa_dims* dims, const sa_route_params* p,
+                   const uint8_t* explicit_map, uint8_t* block_map, float* k_centroid, float* v_centroid,
+                   float* count, double* row_stats, void* workspace, size_t workspace_bytes, bool noalloc,
+                   void* stream) {
   if (const int32_t rc = check_dims(dims, p, v_block_src != nullptr)) return rc;
   sa::KvLayout lay;
   if (const int32_t rc = build_layout(dims, p, &lay)) return rc;
@@ -261,13 +269,29 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
   size_t need = 0;
   if (sol) {
     need = sa::route_workspace_bytes(dims->B, dims->H, dims->Lq / 128, dims->Lkv / p->kblock, dims->d);
-    if (!workspace || workspace_bytes < need)
-      return fail(SA_E_WORKSPACE, "sparse_attn_route: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return fail(SA_E_ALIGN, "sparse_attn_route: workspace must be 256-byte aligned");
+    if (noalloc) {
+      if (need > sa::kRouteScratchBytes)
+        return fail(SA_E_WORKSPACE,
+                    "sparse_attn_route_noalloc: these shapes need %zu bytes of workspace, more than the %zu the "
+                    "library holds per device (SA_ROUTE_SCRATCH_BYTES); call sparse_attn_route with a workspace",
+                    need, (size_t)sa::kRouteScratchBytes);
+    } else {
+      if (!workspace || workspace_bytes < need)
+        return fail(SA_E_WORKSPACE, "sparse_attn_route: workspace of %zu bytes required (got %zu)", need,
+                    workspace_bytes);
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(SA_E_ALIGN, "sparse_attn_route: workspace must be 256-byte aligned");
+    }
   }
-  if (const int32_t rc = check_current_device()) return rc;
+  int dev = 0;
+  if (const int32_t rc = check_current_device(&dev)) return rc;
   if (dims->Lq == 0 || dims->Lkv == 0) return ok();
+  if (sol && noalloc) {
+    const hipError_t e = sa::route_scratch(dev, &workspace);
+    if (e != hipSuccess)
+      return fail(SA_E_DEVICE, "sparse_attn_route_noalloc: no address for the library workspace on device %d: %s",
+                  dev, hipGetErrorString(e));
+  }
   sa::RouteArgs a{};
   a.lay = lay;
   a.q = q; a.k = k; a.k_scale = k_scale; a.v = v; a.v_int8 = v_dtype == SA_INT8; a.v_scale = v_scale;
@@ -287,6 +311,28 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
     a.kdig = reinterpret_cast<int8_t*>(ws + qbytes);
   }
   return launched(sa::launch_route(a, static_cast<hipStream_t>(stream)), "route");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale, const void* v, int32_t v_dtype,
+                          const float* v_scale, const int32_t* v_block_src, const sa_dims* dims,
+                          const sa_route_params* p, const uint8_t* explicit_map, uint8_t* block_map,
+                          float* k_centroid, float* v_centroid, float* count, double* row_stats, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return route_impl(q, k, k_scale, v, v_dtype, v_scale, v_block_src, dims, p, explicit_map, block_map, k_centroid,
+                    v_centroid, count, row_stats, workspace, workspace_bytes, false, stream);
+}
+
+int32_t sparse_attn_route_noalloc(const int8_t* q, const int8_t* k, const float* k_scale, const void* v,
+                                  int32_t v_dtype, const float* v_scale, const int32_t* v_block_src,
+                                  const sa_dims* dims, const sa_route_params* p, const uint8_t* explicit_map,
+                                  uint8_t* block_map, float* k_centroid, float* v_centroid, float* count,
+                                  double* row_stats, void* stream) {
+  return route_impl(q, k, k_scale, v, v_dtype, v_scale, v_block_src, dims, p, explicit_map, block_map, k_centroid,
+                    v_centroid, count, row_stats, nullptr, 0, true, stream);
 }
 
 int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale, const void* v,

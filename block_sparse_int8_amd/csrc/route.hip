@@ -21,6 +21,8 @@
 #include "sa_device.h"
 #include "sa_launch.h"
 
+#include <mutex>
+
 namespace sa {
 
 // Column sums straight from HBM: a lane owns one dword column (4 int8 codes, or
@@ -859,6 +861,34 @@ __global__ __launch_bounds__(256) void decide_explicit_kernel(RouteArgs a) {
     a.stats[(bh * a.nQB + i) * 2] = __builtin_nan("");
     a.stats[(bh * a.nQB + i) * 2 + 1] = __builtin_nan("");
   }
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned route workspace (sparse_attn_route_noalloc), for callers that
+// cannot allocate device memory.  Every device the library runs on holds its
+// own copy until the process ends.  In host code the array's name is not a
+// device address: the address comes from hipGetSymbolAddress, once per device
+// with that device current, and only that address is handed to the kernels.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+void* g_scratch[kScratchDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t route_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 size_t route_workspace_bytes(int B, int H, int nQB, int nKB, int d) {

@@ -144,4 +144,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 // Route workspace layout: qdig then kdig, each 256-byte aligned.
 size_t route_workspace_bytes(int B, int H, int nQB, int nKB, int d);
 
+// The library-owned route workspace of kRouteScratchBytes per device: its
+// device address on device dev (which must be the current device).
+constexpr size_t kRouteScratchBytes = size_t(16) << 20;
+hipError_t route_scratch(int dev, void** ptr);
+
 }  // namespace sa

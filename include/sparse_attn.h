@@ -20,7 +20,9 @@
  * ---------------------------------------
  *  - Device pointers unless a name ends in _host.  The caller allocates and owns
  *    every buffer; the library allocates no device memory and keeps no state
- *    beyond a per-device architecture check and the thread-local error text.
+ *    beyond a per-device architecture check and the thread-local error text
+ *    (sparse_attn_route_noalloc aside: its workspace is a static array of the
+ *    library's device code).
  *  - Work is queued on `stream` (a hipStream_t passed as void*; NULL = the
  *    default stream) and never synchronizes the host.  Arguments are validated
  *    before anything is queued: a non-zero status means nothing was launched.
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 5
+#define SA_ABI_VERSION 6
 
 enum sa_status {
   SA_OK = 0,
@@ -230,6 +232,27 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
                           const uint8_t* explicit_map, uint8_t* block_map, float* k_centroid,
                           float* v_centroid, float* count, double* row_stats, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Bytes of library-owned route workspace per device (sparse_attn_route_noalloc). */
+#define SA_ROUTE_SCRATCH_BYTES (16u << 20)
+
+/* sparse_attn_route for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and errors as sparse_attn_route, without the
+ * workspace: the block sums live in a library-owned device array of
+ * SA_ROUTE_SCRATCH_BYTES (16 MiB), one per device, allocated with the library's
+ * device code when a device first uses it and held until the process ends.
+ * Calls whose sparse_attn_route_workspace_size() exceeds it (more than 85
+ * heads of L = 32768, d = 128, kblock = 64) fail with SA_E_WORKSPACE before anything is
+ * queued.  Nothing is allocated, freed or cleared by the call.  Every call on
+ * one device shares that array: calls that can overlap in time on one device
+ * (other streams, other host threads) race, and the caller must order them.
+ * The array keeps the last call's contents, which no later call reads. */
+int32_t sparse_attn_route_noalloc(const int8_t* q, const int8_t* k, const float* k_scale, const void* v,
+                                  int32_t v_dtype, const float* v_scale, const int32_t* v_block_src,
+                                  const sa_dims* dims, const sa_route_params* p,
+                                  const uint8_t* explicit_map, uint8_t* block_map, float* k_centroid,
+                                  float* v_centroid, float* count, double* row_stats, void* stream);
 
 /* Forward pass over one block map (Configure Sol Sparse Attention, "How it
  * works"; Configure H3 Static Virtual KV, mode list, "residual": centroids share

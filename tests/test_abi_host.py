@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 5
+    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 6
 
 
 def test_missing_library_lists_search_paths(monkeypatch, tmp_path):
