@@ -1,20 +1,32 @@
 """Benchmark of one block-sparse INT8 attention forward on one MI355X.
 
 A step is the whole per-call path on one stream, inputs already resident in HBM:
-quantize_qk_int8(Q, 128-row blocks) -> quantize_qk_int8(K, 64-row blocks) ->
-sparse_attn_route (Sol 1x64, threshold 1.0; or the fixed-sparsity rule with
---rule topk) -> sparse_attn_fwd.
-Workload: B=1, H=40, d=128, L=32768 (21 frames x 30x52 = 32760 valid tokens +
-8 padding rows), per-frame low-rank correlated bf16 Q/K/V (synthetic, seeded).
+quantize_qk_int8(Q, 128-row blocks) -> the K side (quantize_qk_int8(K), the
+INT8 K/V cache append, or the virtual-KV gather) -> sparse_attn_route ->
+sparse_attn_fwd.  The default workload is the measured one:
+B=1, H=40, d=128, L=32768 (21 frames x 30x52 = 32760 valid tokens + 8 padding
+rows), per-frame low-rank correlated bf16 Q/K/V (synthetic, seeded), Sol 1x64
+threshold 1.0.  --config 1..5 picks the other workloads (--config all: one line
+each).
 
-Prints one JSON line.  value = dense-equivalent TOPS = 4*B*H*L*L*d / step time.
+Timing: W warm-up steps, then exactly K back-to-back steps between two device
+synchronizations (ms_per_step, value); HIP events on the same stream bracket
+every stage (their means give the roofline figures).  Then K more steps, each
+after an untimed 1 GiB write that evicts the 256 MB last-level cache, timed by
+events alone: medians with p10 and p90 per stage ("stages_cold_ms").
+
+Prints one JSON line per workload.  value = dense-equivalent TOPS =
+4*B*H*Lq*Lkv*d / step time.  --peaks prints the measured matrix-core and HBM
+ceilings instead.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -31,11 +43,7 @@ PEAK_HBM = 8000.0
 FWD_KERNEL_SOURCES = ["block_sparse_int8_amd/csrc/fwd.hip", "block_sparse_int8_amd/csrc/sa_device.h",
                       "block_sparse_int8_amd/csrc/sa_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_wan14b_c3_traffic.txt")
-
-
-def bf16_dev(bits):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+FLUSH_BYTES = 1 << 30
 
 
 def log(*a):
@@ -67,43 +75,391 @@ def read_traffic(expect_hash: str):
         return None
 
 
-def fwd_algorithmic_ops(bmap: np.ndarray, count: np.ndarray, d: int) -> tuple:
+def fwd_algorithmic_ops(bmap: np.ndarray, count: np.ndarray, d: int, kblock: int = 64) -> tuple:
     """Ops the method itself performs in the forward kernel: per exact
-    (128-query x 64-key) tile 2*128*64*d for QK^T and as many for PV; per
-    centroid column with a non-zero count 2*128*d + 2*128*d.  Returns
-    (ops, exact tiles, centroid columns)."""
-    exact_tiles = float((bmap == 1).sum())
-    cen = (bmap == 2)
-    # columns: per centroid block, the groups with count > 0
-    nz = (count > 0).sum(axis=-1)                      # [B,H,nKB]
-    cols = float((cen * nz[:, :, None, :]).sum())
+    (128-query x 64-key) tile 2*128*64*d for QK^T and as many for PV (a key
+    block of kblock rows is kblock/64 tiles); per centroid column with a
+    non-zero count 2*128*d + 2*128*d.  Returns (ops, exact tiles, centroid
+    columns)."""
+    exact_tiles = float((bmap == 1).sum()) * (kblock // 64)
+    cols = 0.0
+    if count is not None:
+        cen = (bmap == 2)
+        nz = (count > 0).sum(axis=-1)                      # [B,H,nKB]
+        cols = float((cen * nz[:, :, None, :]).sum())
     return exact_tiles * 4.0 * 128 * 64 * d + cols * 4.0 * 128 * d, exact_tiles, cols
 
 
-def cpu_baseline(wl, sample_stride: int):
-    """Time the oracle (as it stands) on the host cores: quantize Q and K and
-    route in full, the forward pass on every sample_stride-th query block,
-    extrapolated to the whole workload."""
+def host_info():
+    """CPU model and logical CPU count of this host."""
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def stats(x):
+    x = np.asarray(x, dtype=np.float64)
+    return {"median": round(float(np.median(x)), 4), "p10": round(float(np.percentile(x, 10)), 4),
+            "p90": round(float(np.percentile(x, 90)), 4)}
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+class Case:
+    """One workload on the device: inputs, preallocated outputs, its stages
+    (name -> callable) in order, the algorithmic bytes of each HBM-bound stage
+    and everything the report needs."""
+
+    def __init__(self, n, args, sa, W, torch):
+        self.n, self.sa, self.torch = n, sa, torch
+        t = time.perf_counter()
+        if n == 3:
+            wl = W.wan_like(H=args.heads)
+        else:
+            wl = W.config(n)
+        if args.rule == "topk" and wl.explicit_map is None:
+            wl.rule, wl.sparsity = 1, args.sparsity
+        wl.qk_float = bool(args.qk_float)
+        if wl.qk_float and wl.v_int8:
+            raise SystemExit("--qk-float needs bf16 V (not the INT8 cache workload)")
+        self.wl = wl
+        log(f"[bench] generated {wl.name}: B={wl.B} H={wl.H} Lq={wl.Lq} Lkv={wl.Lkv} d={wl.d} "
+            f"in {time.perf_counter() - t:.1f}s")
+        dev = torch.device("cuda")
+        bf = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        self.q, self.k, self.v = bf(wl.q), bf(wl.k), bf(wl.v)
+        B, H, Lq, d = self.q.shape
+        Lkv, kb, G = wl.Lkv, wl.kblock, wl.centroids_per_block
+        nQB, nKB = Lq // 128, Lkv // kb
+        self.B, self.H, self.Lq, self.Lkv, self.d, self.kb, self.G = B, H, Lq, Lkv, d, kb, G
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        self.q8, self.qs = e((B, H, Lq, d), torch.int8), e((B, H, nQB), torch.float32)
+        self.k8, self.ks = e((B, H, Lkv, d), torch.int8), e((B, H, Lkv // wl.k_scale_rows), torch.float32)
+        self.vbs = None
+        self.v_in, self.vsc = self.v, None
+        if wl.v_int8:
+            self.v8, self.vsc = e((B, H, Lkv, d), torch.int8), e((B, H, Lkv // wl.v_scale_rows), torch.float32)
+            self.v_in = self.v8
+        if wl.virtual:
+            self.cos = torch.from_numpy(wl.rope_cos).to(dev)
+            self.sin = torch.from_numpy(wl.rope_sin).to(dev)
+        Gs = max(G, 1)
+        self.routed = dict(map=e((B, H, nQB, nKB), torch.uint8), k_centroid=e((B, H, nKB, Gs, d), torch.float32),
+                           v_centroid=e((B, H, nKB, Gs, d), torch.float32), count=e((B, H, nKB, Gs), torch.float32))
+        if G == 0:
+            self.routed = dict(map=self.routed["map"])
+        self.em = None if wl.explicit_map is None else torch.from_numpy(np.ascontiguousarray(wl.explicit_map)).to(dev)
+        self.out = e((B, H, Lq, d), torch.bfloat16)
+        self.ws = None
+        self.stage_names = ["quantize_q", "k_side", "route", "fwd"]
+        # the quantizer writes the codes' column sums and the route reads them
+        # instead of the codes (routing rules and centroids need the sums)
+        self.use_sums = wl.explicit_map is None or G > 0
+        self.qsum = e((B, H, Lq // 128, d), torch.int16) if wl.explicit_map is None else None
+        self.ksum = (e((B, H, Lkv // 32, d), torch.int16) if self.use_sums and not wl.virtual and not wl.v_int8
+                     else None)
+
+    # -- stages ---------------------------------------------------------------
+    def quantize_q(self):
+        self.sa.quantize_qk_int8(self.q, self.wl.lq_valid, 128, out=self.q8, scale=self.qs,
+                                 col_sums=self.qsum if self.qsum is not None else False, sum_rows=128)
+
+    def k_side(self):
+        wl, sa = self.wl, self.sa
+        if wl.virtual:
+            kq, ks, vbs = sa.gather_virtual_kv(self.k, wl.rows_per_slice, wl.src_map.tolist(), self.cos, self.sin,
+                                               wl.rot_offset, wl.k_scale_rows)
+            self.k8, self.ks, self.vbs = kq, ks, vbs
+            return
+        if wl.v_int8:
+            # FlashVSR: K and V kept as an INT8 cache of 128-row slabs; the whole
+            # cache is (re)written here, as the streaming append would over time
+            sa.kv_cache_append_int8(self.k, self.k8, self.ks, 0, wl.lkv_valid, wl.k_scale_rows)
+            sa.kv_cache_append_int8(self.v, self.v8, self.vsc, 0, wl.lkv_valid, wl.v_scale_rows)
+            return
+        sa.quantize_qk_int8(self.k, wl.lkv_valid, wl.k_scale_rows, out=self.k8, scale=self.ks,
+                            col_sums=self.ksum if self.ksum is not None else False, sum_rows=32)
+
+    def route(self):
+        wl = self.wl
+        r = self.sa.sparse_attn_route(self.q8, self.k8, self.ks, self.v_in, lq_valid=wl.lq_valid,
+                                      lkv_valid=wl.lkv_valid, v_scale=self.vsc, v_block_src=self.vbs,
+                                      threshold=wl.threshold, centroids_per_block=self.G,
+                                      prefix_tokens=wl.prefix_tokens, kblock=self.kb, k_scale_rows=wl.k_scale_rows,
+                                      v_scale_rows=wl.v_scale_rows, explicit_map=self.em, map_kblock=wl.map_kblock,
+                                      rule=wl.rule, sparsity=wl.sparsity, workspace=self.ws, outputs=self.routed,
+                                      q_sums=self.qsum if wl.explicit_map is None else None, k_sums=self.ksum)
+        self.ws = r["workspace"]
+
+    def fwd(self):
+        wl, r = self.wl, self.routed
+        kw = dict(k_centroid=r.get("k_centroid"), v_centroid=r.get("v_centroid"), count=r.get("count"),
+                  lq_valid=wl.lq_valid, lkv_valid=wl.lkv_valid, centroids_per_block=self.G, kblock=self.kb,
+                  sm_scale=wl.sm_scale, out_dtype=self.torch.bfloat16, out=self.out)
+        if wl.qk_float:
+            self.sa.sparse_attn_fwd_float(self.q, self.k, self.v, r["map"], v_block_src=self.vbs, **kw)
+        else:
+            self.sa.sparse_attn_fwd(self.q8, self.qs, self.k8, self.ks, self.v_in, r["map"], v_scale=self.vsc,
+                                    v_block_src=self.vbs, k_scale_rows=wl.k_scale_rows,
+                                    v_scale_rows=wl.v_scale_rows, **kw)
+
+    def stages(self):
+        return [self.quantize_q, self.k_side, self.route, self.fwd]
+
+    # -- bytes of the HBM-bound stages ---------------------------------------
+    def hbm_bytes(self):
+        """Bytes each HBM-bound stage must move in this design: reads of its
+        inputs and writes of its outputs, each once.  The quantizer's column
+        sums (int16 per 32 rows, 1/16 of a code tensor) are written by the
+        quantizer and read by the route instead of the codes."""
+        wl, B, H, d = self.wl, self.B, self.H, self.d
+        nQB, nKB = self.Lq // 128, self.Lkv // self.kb
+        qe, ke = B * H * self.Lq * d, B * H * self.Lkv * d
+        qsum_b = qe // 64 if self.qsum is not None else 0
+        ksum_b = ke // 16 if self.ksum is not None else 0
+        out = {"quantize_q": qe * 3 + B * H * nQB * 4 + qsum_b}
+        if wl.virtual:
+            out["k_side"] = B * H * wl.n_phys * wl.rows_per_slice * d * 2 + ke + B * H * (self.Lkv // 64) * 4
+        elif wl.v_int8:
+            out["k_side"] = 2 * (ke * 3 + B * H * (self.Lkv // 128) * 4)
+        else:
+            out["k_side"] = ke * 3 + B * H * (self.Lkv // wl.k_scale_rows) * 4 + ksum_b
+        map_bytes = B * H * nQB * nKB
+        cen = B * H * nKB * self.G * (2 * d + 1) * 4
+        v_bytes = B * H * wl.v.shape[2] * d * (1 if wl.v_int8 else 2)
+        if wl.explicit_map is None:
+            out["route"] = (qsum_b or qe) + (ksum_b or ke) + v_bytes + cen + map_bytes
+        elif self.G > 0:
+            out["route"] = (ksum_b or ke) + v_bytes + cen + 2 * map_bytes
+        else:
+            out["route"] = 2 * map_bytes
+        return out
+
+    def plain_bytes(self):
+        """The bytes the survey's measurement plan assigns to quantizing Q and
+        K and to the route (int8 Q, int8 K and V read by the route, outputs
+        written), for the routed workloads: their sum over the three stages'
+        time is the like-for-like HBM figure whichever stage reads what."""
+        wl, B, H, d = self.wl, self.B, self.H, self.d
+        nQB, nKB = self.Lq // 128, self.Lkv // self.kb
+        qe, ke = B * H * self.Lq * d, B * H * self.Lkv * d
+        quant = qe * 3 + B * H * nQB * 4 + ke * 3 + B * H * (self.Lkv // wl.k_scale_rows) * 4
+        route = qe + ke + B * H * wl.v.shape[2] * d * 2 + B * H * nKB * self.G * (2 * d + 1) * 4 + B * H * nQB * nKB
+        return quant + route
+
+    def workload_desc(self):
+        wl = self.wl
+        rule = (f"top-k sparsity {wl.sparsity:g}" if wl.rule == 1 else
+                "explicit map" if wl.explicit_map is not None else f"threshold {wl.threshold:g}")
+        names = {1: f"tiny Sol 1x64: B=1 H={self.H} d={self.d} L={self.Lq}, {rule}",
+                 2: f"FlashVSR LCSA over an INT8 K/V cache: B=1 H={self.H} d={self.d} L={self.Lq}, 128x128 blocks, "
+                    f"{rule}",
+                 3: f"Wan-14B-like Sol 1x64: B=1 H={self.H} d=128 L=32768 (32760 valid), {rule}",
+                 4: f"Sol 2x32 with 1024-token dense prefix: B=1 H={self.H} d=128 L={self.Lq}, {rule}",
+                 5: f"virtual KV residual: B=1 H={self.H} d=128 Lq={self.Lq} Lkv={self.Lkv} logical, {rule}"}
+        return names[self.n]
+
+
+def cpu_baseline(case, stride: int):
+    """Time the oracle (as it stands) on the host cores: quantization, the
+    K side and the route over the whole workload, the forward pass on every
+    stride-th query block, extrapolated to the whole workload."""
     import oracle
+    wl = case.wl
     t0 = time.perf_counter()
     q8, qs = oracle.quantize(wl.q, wl.lq_valid, 128)
-    k8, ks = oracle.quantize(wl.k, wl.lkv_valid, 64)
+    vbs = None
+    if wl.virtual:
+        k8, ks, vbs = oracle.gather_virtual_kv(wl.k, wl.rows_per_slice, wl.src_map, wl.rope_cos, wl.rope_sin,
+                                               wl.rot_offset, wl.k_scale_rows)
+    else:
+        k8, ks = oracle.quantize(wl.k, wl.lkv_valid, wl.k_scale_rows)
+    vkw = dict(v_bits=wl.v)
+    if wl.v_int8:
+        v8, vs = oracle.quantize(wl.v, wl.lkv_valid, wl.v_scale_rows)
+        vkw = dict(v8=v8, v_scale=vs, v_scale_rows=wl.v_scale_rows)
     t1 = time.perf_counter()
-    r = oracle.route(q8, k8, ks, 64, wl.lq_valid, wl.lkv_valid, v_bits=wl.v, tau=wl.threshold, G=1, kblock=64,
-                     rule=wl.rule, sparsity=wl.sparsity)
+    r = oracle.route(q8, k8, ks, wl.k_scale_rows, wl.lq_valid, wl.lkv_valid, v_block_src=vbs, tau=wl.threshold,
+                     G=wl.centroids_per_block, prefix=wl.prefix_tokens, kblock=wl.kblock,
+                     explicit_map=wl.explicit_map, map_kblock=wl.map_kblock, rule=wl.rule, sparsity=wl.sparsity,
+                     segments=wl.segments, **vkw)
     t2 = time.perf_counter()
     nQB = wl.Lq // 128
     total = wl.B * wl.H * nQB
-    sel = np.arange(0, total, sample_stride, dtype=np.int64)
-    out, lse, _ = oracle.forward(q8, qs, k8, ks, 64, wl.lq_valid, wl.lkv_valid, r["map"], kbar=r["kbar"],
-                                 vbar=r["vbar"], count=r["count"], v_bits=wl.v, kblock=64, G=1,
-                                 sm_scale=wl.sm_scale, sel=sel, q_bits=wl.q if wl.qk_float else None,
-                                 k_bits=wl.k if wl.qk_float else None)
+    sel = np.arange(0, total, stride, dtype=np.int64)
+    out, _, _ = oracle.forward(q8, qs, k8, ks, wl.k_scale_rows, wl.lq_valid, wl.lkv_valid, r["map"], kbar=r["kbar"],
+                               vbar=r["vbar"], count=r["count"], v_block_src=vbs, kblock=wl.kblock,
+                               G=wl.centroids_per_block, sm_scale=wl.sm_scale, sel=sel, segments=wl.segments,
+                               q_bits=wl.q if wl.qk_float else None, k_bits=wl.k if wl.qk_float else None, **vkw)
     t3 = time.perf_counter()
     fwd_full = (t3 - t2) * total / len(sel)
     est = (t1 - t0) + (t2 - t1) + fwd_full
     return dict(est_s=est, quant_s=t1 - t0, route_s=t2 - t1, fwd_sample_s=t3 - t2, nsel=len(sel), total=total,
                 threads=oracle.num_threads(), sel=sel, out=out, map=r["map"], tie=r["tie"])
+
+
+CPU_STRIDE = {1: 1, 2: 1, 3: 40, 4: 24, 5: 1}
+
+
+def run_case(n, args, sa, W, torch):
+    case = Case(n, args, sa, W, torch)
+    stream = torch.cuda.current_stream()
+    stages = case.stages()
+    ns = len(stages)
+
+    def step(ev=None):
+        for i, f in enumerate(stages):
+            if ev is not None:
+                ev[i].record(stream)
+            f()
+        if ev is not None:
+            ev[ns].record(stream)
+
+    if args.calibrate_copy_mib:
+        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done")
+        del src, dst
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # phase A: K back-to-back steps between two synchronizations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    warm = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(ns)] for s in range(args.steps)])
+    ms_step = wall * 1e3 / args.steps
+    stage_mean = warm.mean(axis=0)
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step wall; stages (ms) " +
+        " ".join(f"{nm} {m:.4f}" for nm, m in zip(case.stage_names, stage_mean)))
+    # phase B: K steps, each after an untimed write of FLUSH_BYTES
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        flush.fill_(s & 0xFF)
+        step(evc[s])
+    torch.cuda.synchronize()
+    del flush
+    cold = np.array([[evc[s][i].elapsed_time(evc[s][i + 1]) for i in range(ns)] for s in range(args.steps)])
+    cold_total = cold.sum(axis=1)
+
+    wl = case.wl
+    bmap = case.routed["map"].cpu().numpy()
+    cnt = case.routed["count"].cpu().numpy() if "count" in case.routed else None
+    ops, exact_tiles, cols = fwd_algorithmic_ops(bmap, cnt, case.d, case.kb)
+    fwd_ms = float(stage_mean[3])
+    achieved = ops / (fwd_ms * 1e-3) / 1e12
+    # The exact tiles do as many int8 ops (QK^T) as bf16 flops (PV), so the
+    # kernel's ceiling is the harmonic combination of the two peaks.
+    peak_mixed = 1.0 / (0.5 / PEAK_INT8 + 0.5 / PEAK_BF16)
+    if wl.qk_float:
+        peak_mixed = PEAK_BF16   # both products on bf16 matrix cores
+    khash = kernel_hash()
+    headline = n == 3 and not wl.qk_float and wl.rule == 0 and case.H == 40
+    traffic = read_traffic(khash) if headline else None   # counters were taken on the headline workload
+    dense_ops = 4.0 * case.B * case.H * case.Lq * case.Lkv * case.d
+    value = dense_ops / (ms_step * 1e-3) / 1e12
+    nvalid_blocks = -(-wl.lkv_valid // case.kb)
+    kept = float((bmap[..., :nvalid_blocks] == 1).mean())
+    if n == 3:
+        metric = METRIC if wl.rule == 0 else METRIC.replace("thr=1.0", f"top-k sparsity={wl.sparsity:g}")
+        if wl.qk_float:
+            metric += ", bf16 QK"
+    else:
+        metric = f"sparse attn fwd ms + dense-equiv TOPS, workload {n} ({W.CONFIG_NAMES[n]})"
+    res = {
+        "metric": metric,
+        "value": round(value, 3),
+        "unit": "dense-equiv TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 QK^T + fp32 softmax + bf16 PV" if wl.qk_float else "int8 QK^T + fp32 softmax + bf16 PV",
+        "data": "synthetic (seeded bf16 Q/K/V; " + ("per-frame low-rank correlated)" if n in (3, 4) else "N(0,1))"),
+        "config": {"workload": case.workload_desc(), "B": case.B, "H": case.H, "Lq": case.Lq, "Lkv": case.Lkv,
+                   "d": case.d, "lq_valid": wl.lq_valid, "lkv_valid": wl.lkv_valid, "kblock": case.kb,
+                   "centroids": {0: "none", 1: "1x64", 2: "2x32"}[case.G],
+                   "rule": "explicit" if wl.explicit_map is not None else ("topk" if wl.rule == 1 else "threshold"),
+                   "threshold": wl.threshold if wl.explicit_map is None and wl.rule == 0 else None,
+                   "sparsity": wl.sparsity if wl.rule == 1 else None, "out_dtype": "bf16",
+                   "parallelism": "single GPU"},
+        "stages_ms": {nm: round(float(m), 4) for nm, m in zip(case.stage_names, stage_mean)},
+        "stages_cold_ms": {**{nm: stats(cold[:, i]) for i, nm in enumerate(case.stage_names)},
+                           "step": stats(cold_total)},
+        "routing": {"kept_fraction": round(kept, 5), "exact_tiles": int(exact_tiles), "centroid_columns": int(cols),
+                    "map_entries": int(bmap.size)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak_mixed, 2),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak_mixed, 4), "traffic": traffic,
+                     "kernel": ("sparse_attn_fwd_float (fwd_kernel<%d,true,false,true>)" % case.d if wl.qk_float
+                                else "sparse_attn_fwd (fwd_kernel<%d,false,%s,true>)" % (
+                                    case.d, "true" if wl.v_int8 else "false")),
+                     "ops_per_launch": ops, "fwd_ms_mean": round(fwd_ms, 4),
+                     "frac_of_int8_peak": round(achieved / PEAK_INT8, 4), "kernel_hash": khash},
+        "hbm_kernels": {},
+    }
+    for nm, nbytes in case.hbm_bytes().items():
+        i = case.stage_names.index(nm)
+        gbs = nbytes / (stage_mean[i] * 1e-3) / 1e9
+        res["hbm_kernels"][nm] = {"bytes": int(nbytes), "GB/s": round(gbs, 1),
+                                  "frac_of_8TB/s": round(gbs / PEAK_HBM, 4)}
+    if wl.explicit_map is None and not wl.virtual:
+        nbytes = case.plain_bytes()
+        ms3 = float(stage_mean[0] + stage_mean[1] + stage_mean[2])
+        gbs = nbytes / (ms3 * 1e-3) / 1e9
+        res["hbm_kernels"]["quantize_q+k_side+route"] = {"bytes": int(nbytes), "ms": round(ms3, 4),
+                                                         "GB/s": round(gbs, 1), "frac_of_8TB/s": round(gbs / PEAK_HBM, 4)}
+
+    if not args.no_cpu_baseline:
+        stride = args.cpu_sample_stride or CPU_STRIDE[n]
+        log(f"[bench] timing the CPU oracle on a sample (every {stride}th query block) ...")
+        cb = cpu_baseline(case, stride)
+        model, ncpu = host_info()
+        res["cpu_baseline"] = {
+            "value": round(dense_ops / cb["est_s"] / 1e12, 6), "unit": "dense-equiv TOPS", "cores": cb["threads"],
+            "kind": "oracle", "cpu_model": model, "nproc": ncpu,
+            "sample": (f"quantize, K side and route over the whole workload ({cb['quant_s'] + cb['route_s']:.1f}s), "
+                       f"forward on {cb['nsel']} of {cb['total']} query blocks (every {stride}th, "
+                       f"{cb['fwd_sample_s']:.1f}s) scaled by {cb['total'] / cb['nsel']:.0f}x; "
+                       f"estimated {cb['est_s']:.1f}s per forward"),
+            "ms_per_step_est": round(cb["est_s"] * 1e3, 1)}
+        # spot parity on the sampled blocks (same inputs, maps compared first)
+        B, H, Lq, d = case.B, case.H, case.Lq, case.d
+        nQB, nKB = Lq // 128, case.Lkv // case.kb
+        gout = case.out.float().cpu().numpy().reshape(B * H, Lq, d)
+        mism = int(((bmap != cb["map"]) & (cb["tie"] == 0)).sum())
+        errs = []
+        gm, om = bmap.reshape(B * H, nQB, nKB), cb["map"].reshape(B * H, nQB, nKB)
+        for e, sid in enumerate(cb["sel"]):
+            bh, i = divmod(int(sid), nQB)
+            if (gm[bh, i] != om[bh, i]).any():
+                continue
+            r1 = min(128, max(0, wl.lq_valid - i * 128))
+            errs.append(np.abs(gout[bh, i * 128:i * 128 + r1] - cb["out"][e, :r1]).reshape(-1))
+        err = np.concatenate(errs) if errs else np.zeros(1)
+        res["parity_sample"] = {"map_mismatches_outside_ties": mism, "ties": int(cb["tie"].sum()),
+                                "max_abs": float(err.max()), "mean_abs": float(err.mean()), "out_dtype": "bf16"}
+    print(json.dumps(res), flush=True)
+    del case
+    torch.cuda.empty_cache()
 
 
 def bench_cache_append(args, sa, W):
@@ -164,22 +520,101 @@ def bench_cache_append(args, sa, W):
     print(json.dumps(res), flush=True)
 
 
+def bench_peaks(args):
+    """Matrix-core throughput (int8, bf16 and the forward's 50/50 mix, on
+    random operands) and HBM read / write / copy bandwidth, measured with the
+    probe kernels of libsa_probe.so."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_int8_amd", "libsa_probe.so"))
+    lib.sa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p]
+    lib.sa_probe_bandwidth.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    g = torch.Generator().manual_seed(7)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (64 * 256,), dtype=torch.int64, generator=g).to(torch.int32).cuda()
+    blocks = 256 * 8                       # 8 workgroups of 4 waves per CU: 8 waves per SIMD
+    sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
+    iters = 4096
+    res = {"metric": "MI355X measured ceilings (probe kernels)", "unit": "TOP/s | GB/s", "n_gpus": 1}
+    # ops per MFMA: int8 32x32x32 = 2*32768, bf16 32x32x16 = 2*16384
+    per_wave = {0: iters * 4 * 65536, 1: iters * 4 * 32768, 2: iters * (2 * 65536 + 4 * 32768)}
+    names = {0: "int8_mfma_TOPS", 1: "bf16_mfma_TFLOPS", 2: "mixed_50_50_TOPS"}
+    for mode in (0, 1, 2):
+        best = []
+        for rep in range(3 + args.warmup):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert lib.sa_probe_mfma(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(sink.data_ptr()), mode, iters,
+                                     blocks, sp) == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep >= args.warmup:
+                best.append(e0.elapsed_time(e1))
+        ms = float(np.median(best))
+        res[names[mode]] = round(per_wave[mode] * blocks * 4 / (ms * 1e-3) / 1e12, 1)
+        log(f"[peaks] {names[mode]}: {res[names[mode]]} ({ms:.3f} ms)")
+    nbytes = 2 << 30
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+    y = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for kind, nm, mult in ((0, "hbm_read_GBps", 1), (1, "hbm_write_GBps", 1), (2, "hbm_copy_GBps", 2)):
+        ts = []
+        for rep in range(3 + args.warmup):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert lib.sa_probe_bandwidth(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), nbytes, kind,
+                                          256 * 16, ctypes.c_void_p(sink.data_ptr()), sp) == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep >= args.warmup:
+                ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        res[nm] = round(nbytes * mult / (ms * 1e-3) / 1e9, 1)
+        log(f"[peaks] {nm}: {res[nm]} ({ms:.3f} ms for {nbytes >> 20} MiB)")
+    # torch's own copy and fill kernels on the same buffers, for comparison
+    for nm, fn, mult in (("torch_copy_GBps", lambda: y.copy_(x), 2), ("torch_fill_GBps", lambda: y.fill_(5), 1)):
+        ts = []
+        for rep in range(3 + args.warmup):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep >= args.warmup:
+                ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        res[nm] = round(nbytes * mult / (ms * 1e-3) / 1e9, 1)
+        log(f"[peaks] {nm}: {res[nm]} ({ms:.3f} ms)")
+    m8, mb = res["int8_mfma_TOPS"], res["bf16_mfma_TFLOPS"]
+    res["mixed_harmonic_TOPS"] = round(1.0 / (0.5 / m8 + 0.5 / mb), 1)
+    res["datasheet"] = {"int8_TOPS": PEAK_INT8, "bf16_TFLOPS": PEAK_BF16, "hbm_GBps": PEAK_HBM,
+                        "mixed_harmonic_TOPS": round(1.0 / (0.5 / PEAK_INT8 + 0.5 / PEAK_BF16), 1)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="3",
+                    help="workload 1..5 (3 is the measured one; the others are the parity workloads), or 'all'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-stride", type=int, default=40)
-    ap.add_argument("--heads", type=int, default=40, help="heads (40 for the measured workload)")
+    ap.add_argument("--cpu-sample-stride", type=int, default=0,
+                    help="oracle forward on every n-th query block (0: a per-workload default)")
+    ap.add_argument("--heads", type=int, default=40, help="heads of workload 3 (40 for the measured workload)")
     ap.add_argument("--rule", choices=["threshold", "topk"], default="threshold",
-                    help="routing rule: Sol threshold 1.0 (the measured workload) or fixed sparsity")
+                    help="routing rule for the routed workloads: Sol threshold (the measured workload) or fixed "
+                         "sparsity")
     ap.add_argument("--sparsity", type=float, default=0.75, help="pruned fraction for --rule topk")
     ap.add_argument("--qk-float", action="store_true",
                     help="exact tiles on the floating path (bf16 QK^T) instead of INT8 (same map and centroids)")
     ap.add_argument("--cache-append", action="store_true",
                     help="measure the streaming INT8 K/V cache append instead (FlashVSR-like: H=12, frames of "
                          "2048 rows, a ring of four frames)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the matrix-core and HBM ceilings with the probe kernels instead")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scales HBM counters under rocprofv3)")
     args = ap.parse_args()
@@ -193,164 +628,15 @@ def main():
     import workloads as W
 
     sa.device_check(0)
+    if args.peaks:
+        bench_peaks(args)
+        return
     if args.cache_append:
         bench_cache_append(args, sa, W)
         return
-    t = time.perf_counter()
-    wl = W.wan_like(H=args.heads)
-    topk = args.rule == "topk"
-    if topk:
-        wl.rule, wl.sparsity = 1, args.sparsity
-    wl.qk_float = args.qk_float
-    log(f"[bench] generated {wl.name}: B={wl.B} H={wl.H} L={wl.Lq} d={wl.d} in {time.perf_counter() - t:.1f}s")
-    q, k, v = bf16_dev(wl.q), bf16_dev(wl.k), bf16_dev(wl.v)
-    B, H, L, d = q.shape
-    nQB, nKB = L // 128, L // 64
-    dev = q.device
-    stream = torch.cuda.current_stream()
-    # outputs and workspace allocated once, outside the timed region
-    q8 = torch.empty((B, H, L, d), dtype=torch.int8, device=dev)
-    qs = torch.empty((B, H, nQB), dtype=torch.float32, device=dev)
-    k8 = torch.empty((B, H, L, d), dtype=torch.int8, device=dev)
-    ks = torch.empty((B, H, nKB), dtype=torch.float32, device=dev)
-    routed = dict(map=torch.empty((B, H, nQB, nKB), dtype=torch.uint8, device=dev),
-                  k_centroid=torch.empty((B, H, nKB, 1, d), dtype=torch.float32, device=dev),
-                  v_centroid=torch.empty((B, H, nKB, 1, d), dtype=torch.float32, device=dev),
-                  count=torch.empty((B, H, nKB, 1), dtype=torch.float32, device=dev))
-    out = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=dev)
-    ws = None
-
-    def step(ev=None):
-        nonlocal ws
-        if ev: ev[0].record(stream)
-        sa.quantize_qk_int8(q, wl.lq_valid, 128, out=q8, scale=qs)
-        if ev: ev[1].record(stream)
-        sa.quantize_qk_int8(k, wl.lkv_valid, 64, out=k8, scale=ks)
-        if ev: ev[2].record(stream)
-        r = sa.sparse_attn_route(q8, k8, ks, v, lq_valid=wl.lq_valid, lkv_valid=wl.lkv_valid,
-                                 threshold=wl.threshold, centroids_per_block=1, kblock=64, workspace=ws,
-                                 rule=wl.rule, sparsity=wl.sparsity, outputs=routed)
-        ws = r["workspace"]
-        if ev: ev[3].record(stream)
-        if args.qk_float:
-            sa.sparse_attn_fwd_float(q, k, v, routed["map"], k_centroid=routed["k_centroid"],
-                                     v_centroid=routed["v_centroid"], count=routed["count"], lq_valid=wl.lq_valid,
-                                     lkv_valid=wl.lkv_valid, centroids_per_block=1, kblock=64,
-                                     sm_scale=wl.sm_scale, out_dtype=torch.bfloat16, out=out)
-        else:
-            sa.sparse_attn_fwd(q8, qs, k8, ks, v, routed["map"], k_centroid=routed["k_centroid"],
-                               v_centroid=routed["v_centroid"], count=routed["count"], lq_valid=wl.lq_valid,
-                               lkv_valid=wl.lkv_valid, centroids_per_block=1, kblock=64, sm_scale=wl.sm_scale,
-                               out_dtype=torch.bfloat16, out=out)
-        if ev: ev[4].record(stream)
-
-    if args.calibrate_copy_mib:
-        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done")
-        del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stage = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(4)] for s in range(args.steps)])
-    ms_step = wall * 1e3 / args.steps
-    stage_ms = stage.mean(axis=0)
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step wall; stages (ms) quantQ {stage_ms[0]:.3f} "
-        f"quantK {stage_ms[1]:.3f} route {stage_ms[2]:.3f} fwd {stage_ms[3]:.3f}")
-
-    bmap = routed["map"].cpu().numpy()
-    cnt = routed["count"].cpu().numpy()
-    ops, exact_tiles, cols = fwd_algorithmic_ops(bmap, cnt, d)
-    fwd_ms = float(stage_ms[3])
-    achieved = ops / (fwd_ms * 1e-3) / 1e12
-    # The exact tiles do as many int8 ops (QK^T) as bf16 flops (PV), so the
-    # kernel's ceiling is the harmonic combination of the two peaks.
-    peak_mixed = 1.0 / (0.5 / PEAK_INT8 + 0.5 / PEAK_BF16)
-    if args.qk_float:
-        peak_mixed = PEAK_BF16   # both products on bf16 matrix cores
-    khash = kernel_hash()
-    traffic = None if args.qk_float else read_traffic(khash)   # counters were taken on the INT8 kernel
-    elems = B * H * L * d
-    quant_bytes = elems * 2 + elems * 1 + B * H * nQB * 4
-    dense_ops = 4.0 * B * H * L * L * d
-    value = dense_ops / (ms_step * 1e-3) / 1e12
-    valid_blocks = -(-wl.lkv_valid // 64)
-    kept = float((bmap[..., :valid_blocks] == 1).mean())
-    rule_desc = f"top-k sparsity {wl.sparsity:g}" if topk else f"threshold {wl.threshold:g}"
-    res = {
-        "metric": (METRIC if not topk else METRIC.replace("thr=1.0", f"top-k sparsity={wl.sparsity:g}"))
-                  + (", bf16 QK" if args.qk_float else ""),
-        "value": round(value, 3),
-        "unit": "dense-equiv TOPS",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16 QK^T + fp32 softmax + bf16 PV" if args.qk_float else "int8 QK^T + fp32 softmax + bf16 PV",
-        "data": "synthetic (seeded per-frame low-rank correlated bf16 Q/K/V)",
-        "config": {"workload": f"Wan-14B-like Sol 1x64: B=1 H={H} d=128 L=32768 (32760 valid), {rule_desc}",
-                   "B": B, "H": H, "L": L, "d": d, "valid": wl.lkv_valid, "kblock": 64, "centroids": "1x64",
-                   "rule": args.rule, "threshold": wl.threshold, "sparsity": wl.sparsity if topk else None,
-                   "out_dtype": "bf16", "parallelism": "single GPU"},
-        "stages_ms": {"quantize_q": round(float(stage_ms[0]), 4), "quantize_k": round(float(stage_ms[1]), 4),
-                      "route": round(float(stage_ms[2]), 4), "fwd": round(fwd_ms, 4)},
-        "routing": {"kept_fraction": round(kept, 5), "exact_tiles": int(exact_tiles), "centroid_columns": int(cols),
-                    "map_entries": int(bmap.size)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak_mixed, 2),
-                     "unit": "TFLOP/s", "frac": round(achieved / peak_mixed, 4), "traffic": traffic,
-                     "kernel": ("sparse_attn_fwd_float (fwd_kernel<128,true,false,true>)" if args.qk_float
-                                else "sparse_attn_fwd (fwd_kernel<128,false,false,true>)"),
-                     "frac_of_int8_peak": round(achieved / PEAK_INT8, 4), "kernel_hash": khash},
-        "hbm_kernels": {
-            "quantize_qk_int8": {"bytes": quant_bytes,
-                                 "GB/s": round(quant_bytes / (0.5 * (stage_ms[0] + stage_ms[1]) * 1e-3) / 1e9, 1),
-                                 "frac_of_8TB/s": round(quant_bytes / (0.5 * (stage_ms[0] + stage_ms[1]) * 1e-3)
-                                                        / 1e9 / PEAK_HBM, 4)},
-        },
-    }
-    route_bytes = elems * 1 * 2 + elems * 2 + B * H * nKB * d * 4 * 2 + bmap.size
-    res["hbm_kernels"]["sparse_attn_route"] = {
-        "bytes": route_bytes, "GB/s": round(route_bytes / (stage_ms[2] * 1e-3) / 1e9, 1),
-        "frac_of_8TB/s": round(route_bytes / (stage_ms[2] * 1e-3) / 1e9 / PEAK_HBM, 4)}
-
-    if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle on a sample (every {args.cpu_sample_stride}th query block) ...")
-        cb = cpu_baseline(wl, args.cpu_sample_stride)
-        cpu_tops = dense_ops / cb["est_s"] / 1e12
-        res["cpu_baseline"] = {
-            "value": round(cpu_tops, 6), "unit": "dense-equiv TOPS", "cores": cb["threads"], "kind": "oracle",
-            "sample": (f"quantize Q/K and route over the whole workload ({cb['quant_s'] + cb['route_s']:.1f}s), "
-                       f"forward on {cb['nsel']} of {cb['total']} query blocks (every "
-                       f"{args.cpu_sample_stride}th, {cb['fwd_sample_s']:.1f}s) scaled by {cb['total'] / cb['nsel']:.0f}x; "
-                       f"estimated {cb['est_s']:.1f}s per forward"),
-            "ms_per_step_est": round(cb["est_s"] * 1e3, 1)}
-        # spot parity on the sampled blocks (same inputs, maps compared first)
-        gout = out.float().cpu().numpy().reshape(B * H, L, d)
-        mism = int(((bmap != cb["map"]) & (cb["tie"] == 0)).sum())
-        errs = []
-        for e, sid in enumerate(cb["sel"]):
-            bh, i = divmod(int(sid), nQB)
-            if (bmap.reshape(B * H, nQB, nKB)[bh, i] != cb["map"].reshape(B * H, nQB, nKB)[bh, i]).any():
-                continue
-            r1 = min(128, max(0, wl.lq_valid - i * 128))
-            errs.append(np.abs(gout[bh, i * 128:i * 128 + r1] - cb["out"][e, :r1]).reshape(-1))
-        e = np.concatenate(errs) if errs else np.zeros(1)
-        res["parity_sample"] = {"map_mismatches_outside_ties": mism, "ties": int(cb["tie"].sum()),
-                                "max_abs": float(e.max()), "mean_abs": float(e.mean()), "out_dtype": "bf16"}
-    print(json.dumps(res), flush=True)
+    configs = [1, 2, 3, 4, 5] if args.config == "all" else [int(args.config)]
+    for n in configs:
+        run_case(n, args, sa, W, torch)
 
 
 if __name__ == "__main__":

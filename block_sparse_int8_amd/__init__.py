@@ -23,7 +23,7 @@ from typing import Optional, Sequence
 
 import torch
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 SA_OK, SA_E_NULL, SA_E_SHAPE, SA_E_ALIGN, SA_E_VALUE, SA_E_UNSUPPORTED, SA_E_DEVICE, SA_E_LAUNCH, SA_E_WORKSPACE = range(9)
 SA_DROP, SA_EXACT, SA_CENTROID = 0, 1, 2
 SA_BF16, SA_INT8, SA_F32 = 0, 1, 2
@@ -86,15 +86,15 @@ def load(path: Optional[str] = None):
     P = ctypes.POINTER
     lib.sa_device_check.argtypes = [i32]
     lib.sa_device_check.restype = i32
-    lib.quantize_qk_int8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.quantize_qk_int8.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp]
     lib.quantize_qk_int8.restype = i32
     lib.sparse_attn_route_workspace_size.argtypes = [P(sa_dims), P(sa_route_params), i32]
     lib.sparse_attn_route_workspace_size.restype = ctypes.c_size_t
-    lib.sparse_attn_route.argtypes = [vp, vp, vp, vp, i32, vp, vp, P(sa_dims), P(sa_route_params), vp, vp, vp, vp,
-                                      vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sparse_attn_route.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, P(sa_dims), P(sa_route_params), vp, vp,
+                                      vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sparse_attn_route.restype = i32
-    lib.sparse_attn_route_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, vp, P(sa_dims), P(sa_route_params), vp, vp,
-                                              vp, vp, vp, vp, vp]
+    lib.sparse_attn_route_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, P(sa_dims), P(sa_route_params),
+                                              vp, vp, vp, vp, vp, vp, vp]
     lib.sparse_attn_route_noalloc.restype = i32
     lib.sparse_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, P(sa_dims), P(sa_route_params), vp, vp, vp, vp,
                                     f32, vp, i32, vp, vp]
@@ -166,8 +166,13 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, contiguous
 
 
 def quantize_qk_int8(x: torch.Tensor, valid_len: Optional[int] = None, rows_per_block: int = 128,
-                     out: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None, stream=None):
-    """bf16 [B,H,L,d] (any strides over B, H, L) -> (int8 [B,H,L,d], fp32 [B,H,L/R])."""
+                     out: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None, stream=None,
+                     col_sums=False, sum_rows: Optional[int] = None):
+    """bf16 [B,H,L,d] (any strides over B, H, L) -> (int8 [B,H,L,d], fp32 [B,H,L/R]).
+    ``col_sums`` True (or an int16 [B,H,L/sum_rows,d] tensor) also writes the
+    codes' column sums per chunk of ``sum_rows`` rows (32 or rows_per_block;
+    default: rows_per_block for 128-row blocks, the route's Q sums, else 32,
+    the route's K sums) and returns them as a third element."""
     if x.dim() != 4:
         raise ValueError("x must be [B,H,L,d]")
     _need(x, "x", torch.bfloat16, contiguous=False)
@@ -181,10 +186,17 @@ def quantize_qk_int8(x: torch.Tensor, valid_len: Optional[int] = None, rows_per_
         scale = torch.empty((B, H, L // rows_per_block if rows_per_block else 0), dtype=torch.float32, device=x.device)
     _need(out, "out", torch.int8, (B, H, L, d))
     _need(scale, "scale", torch.float32, (B, H, L // rows_per_block))
+    sums = None
+    if sum_rows is None:
+        sum_rows = 128 if rows_per_block == 128 else 32
+    if col_sums is not False and col_sums is not None:
+        sums = col_sums if isinstance(col_sums, torch.Tensor) else torch.empty(
+            (B, H, L // sum_rows, d), dtype=torch.int16, device=x.device)
+        _need(sums, "col_sums", torch.int16, (B, H, L // sum_rows, d))
     _check(load().quantize_qk_int8(_ptr(x), x.stride(0), x.stride(1), x.stride(2), B, H, L, d, valid_len,
-                                   rows_per_block, _ptr(out), _ptr(scale), _stream(stream)))
-    _keep_for(stream, out, scale)
-    return out, scale
+                                   rows_per_block, _ptr(out), _ptr(scale), _ptr(sums), sum_rows, _stream(stream)))
+    _keep_for(stream, out, scale, sums)
+    return (out, scale) if sums is None else (out, scale, sums)
 
 
 def kv_cache_append_int8(x: torch.Tensor, cache_q: torch.Tensor, cache_scale: torch.Tensor, first_slot: int,
@@ -234,12 +246,16 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
                       explicit_map: Optional[torch.Tensor] = None, map_kblock: Optional[int] = None,
                       rule: int = SA_RULE_THRESHOLD, sparsity: float = 0.0, segments=None,
                       row_stats: bool = False, workspace: Optional[torch.Tensor] = None,
-                      outputs: Optional[dict] = None, noalloc: bool = False, stream=None) -> dict:
+                      outputs: Optional[dict] = None, noalloc: bool = False,
+                      q_sums: Optional[torch.Tensor] = None, k_sums: Optional[torch.Tensor] = None,
+                      stream=None) -> dict:
     """Block map + centroids.  ``rule`` picks the threshold rule (``threshold``)
     or the fixed-sparsity rule (``sparsity``); ``segments`` ((start, rows,
     routed) triples) gives a segmented key layout in place of the prefix.
     Returns dict(map, k_centroid, v_centroid, count, row_stats) with the shapes
-    of sparse_attn.h.  ``noalloc`` calls sparse_attn_route_noalloc (library-owned
+    of sparse_attn.h.  ``q_sums`` / ``k_sums``: the column sums quantize_qk_int8
+    returned with q8 / k8 (the route then reads the sums, not the codes).
+    ``noalloc`` calls sparse_attn_route_noalloc (library-owned
     workspace; pass every output in ``outputs`` for a call that allocates
     nothing)."""
     B, H, Lq, d = q8.shape
@@ -259,6 +275,10 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
         _need(v_scale, "v_scale", torch.float32, (B, H, Lv // v_scale_rows))
     if v_block_src is not None:
         _need(v_block_src, "v_block_src", torch.int32, (Lkv // 64,))
+    if q_sums is not None:
+        _need(q_sums, "q_sums", torch.int16, (B, H, Lq // 128, d))
+    if k_sums is not None:
+        _need(k_sums, "k_sums", torch.int16, (B, H, Lkv // 32, d))
     nQB, nKB = Lq // 128, Lkv // kblock
     if explicit_map is not None:
         _need(explicit_map, "explicit_map", torch.uint8, (B, H, nQB, Lkv // map_kblock))
@@ -287,7 +307,8 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
         _need(stats, "row_stats", torch.float64, (B, H, nQB, 2))
     if noalloc:
         _check(lib.sparse_attn_route_noalloc(_ptr(q8), _ptr(k8), _ptr(k_scale), _ptr(v), v_dtype, _ptr(v_scale),
-                                             _ptr(v_block_src), ctypes.byref(dims), ctypes.byref(prm),
+                                             _ptr(v_block_src), _ptr(q_sums), _ptr(k_sums), ctypes.byref(dims),
+                                             ctypes.byref(prm),
                                              _ptr(explicit_map), _ptr(bmap), _ptr(kc), _ptr(vc), _ptr(cnt),
                                              _ptr(stats), _stream(stream)))
         _keep_for(stream, bmap, kc, vc, cnt, stats)
@@ -303,7 +324,8 @@ def sparse_attn_route(q8: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
         ws_ptr = ctypes.c_void_p(base + off)
         ws_avail = workspace.numel() - off
     _check(lib.sparse_attn_route(_ptr(q8), _ptr(k8), _ptr(k_scale), _ptr(v), v_dtype, _ptr(v_scale),
-                                 _ptr(v_block_src), ctypes.byref(dims), ctypes.byref(prm), _ptr(explicit_map),
+                                 _ptr(v_block_src), _ptr(q_sums), _ptr(k_sums), ctypes.byref(dims),
+                                 ctypes.byref(prm), _ptr(explicit_map),
                                  _ptr(bmap), _ptr(kc), _ptr(vc), _ptr(cnt), _ptr(stats), ws_ptr, ws_avail,
                                  _stream(stream)))
     _keep_for(stream, bmap, kc, vc, cnt, stats, workspace)
@@ -450,9 +472,10 @@ def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, lq_va
     Lq, Lkv = q.shape[2], k.shape[2]
     lq_valid = Lq if lq_valid is None else lq_valid
     lkv_valid = Lkv if lkv_valid is None else lkv_valid
-    q8, qs = quantize_qk_int8(q, lq_valid, 128, stream=stream)
-    k8, ks = quantize_qk_int8(k, lkv_valid, kblock, stream=stream)
-    r = sparse_attn_route(q8, k8, ks, v, lq_valid=lq_valid, lkv_valid=lkv_valid, threshold=threshold,
+    q8, qs, qsum = quantize_qk_int8(q, lq_valid, 128, stream=stream, col_sums=True, sum_rows=128)
+    k8, ks, ksum = quantize_qk_int8(k, lkv_valid, kblock, stream=stream, col_sums=True, sum_rows=32)
+    r = sparse_attn_route(q8, k8, ks, v, q_sums=qsum, k_sums=ksum, lq_valid=lq_valid, lkv_valid=lkv_valid,
+                          threshold=threshold,
                           centroids_per_block=centroids_per_block, prefix_tokens=prefix_tokens, kblock=kblock,
                           explicit_map=explicit_map, map_kblock=map_kblock, rule=rule, sparsity=sparsity,
                           segments=segments, stream=stream)

@@ -176,7 +176,7 @@ int32_t sa_device_check(int32_t device) {
 
 int32_t quantize_qk_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL, int32_t B, int32_t H,
                          int32_t L, int32_t d, int32_t valid_len, int32_t rows_per_block, int8_t* x_q,
-                         float* scale, void* stream) {
+                         float* scale, int16_t* col_sums, int32_t sum_rows, void* stream) {
   if (!x_bf16 || !x_q || !scale) return fail(SA_E_NULL, "quantize_qk_int8: x, x_q and scale must not be NULL");
   if (B < 1 || H < 1 || L < 0) return fail(SA_E_SHAPE, "quantize_qk_int8: bad B/H/L (%d, %d, %d)", B, H, L);
   if (d != 64 && d != 128) return fail(SA_E_SHAPE, "quantize_qk_int8: d must be 64 or 128 (got %d)", d);
@@ -187,10 +187,13 @@ int32_t quantize_qk_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL,
   if (!aligned16(x_bf16) || !aligned16(x_q)) return fail(SA_E_ALIGN, "quantize_qk_int8: x and x_q must be 16-byte aligned");
   if (sB % 8 || sH % 8 || sL % 8 || sL < d)
     return fail(SA_E_ALIGN, "quantize_qk_int8: strides must be multiples of 8 elements and sL >= d");
+  if (col_sums && !aligned16(col_sums)) return fail(SA_E_ALIGN, "quantize_qk_int8: col_sums must be 16-byte aligned");
+  if (col_sums && sum_rows != 32 && sum_rows != rows_per_block)
+    return fail(SA_E_VALUE, "quantize_qk_int8: sum_rows must be 32 or rows_per_block (got %d)", sum_rows);
   if (const int32_t rc = check_current_device()) return rc;
   if (L == 0) return ok();
   sa::QuantizeArgs a{static_cast<const uint16_t*>(x_bf16), sB, sH, sL, B, H, L, d, valid_len, rows_per_block, x_q, scale,
-                     L / rows_per_block, 0};
+                     L / rows_per_block, 0, col_sums, col_sums ? sum_rows : 32};
   return launched(sa::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize");
 }
 
@@ -215,7 +218,7 @@ int32_t kv_cache_append_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t
   if (const int32_t rc = check_current_device()) return rc;
   if (rows == 0) return ok();
   sa::QuantizeArgs a{static_cast<const uint16_t*>(x_bf16), sB, sH, sL, B, H, rows, d, valid_len, rows_per_slab, cache_q,
-                     cache_scale, slots, first_slot};
+                     cache_scale, slots, first_slot, nullptr, 32};
   return launched(sa::launch_quantize(a, static_cast<hipStream_t>(stream)), "kv_cache_append_int8");
 }
 
@@ -233,15 +236,18 @@ namespace {
 // sparse_attn_route_noalloc (library-owned workspace: `noalloc` set, and
 // workspace / workspace_bytes ignored).
 int32_t route_impl(const int8_t* q, const int8_t* k, const float* k_scale, const void* v, int32_t v_dtype,
-                   const float* v_scale, const int32_t* v_block_src, const sa_dims* dims, const sa_route_params* p,
+                   const float* v_scale, const int32_t* v_block_src, const int16_t* q_sums, const int16_t* k_sums,
+                   const sa_dims* dims, const sa_route_params* p,
                    const uint8_t* explicit_map, uint8_t* block_map, float* k_centroid, float* v_centroid,
                    float* count, double* row_stats, void* workspace, size_t workspace_bytes, bool noalloc,
                    void* stream) {
   if (const int32_t rc = check_dims(dims, p, v_block_src != nullptr)) return rc;
   sa::KvLayout lay;
   if (const int32_t rc = build_layout(dims, p, &lay)) return rc;
-  if (!q || !k || !k_scale || !block_map) return fail(SA_E_NULL, "sparse_attn_route: q, k, k_scale and block_map are required");
-  if (!aligned16(q) || !aligned16(k)) return fail(SA_E_ALIGN, "sparse_attn_route: q and k must be 16-byte aligned");
+  if ((!q && !q_sums) || (!k && !k_sums) || !k_scale || !block_map)
+    return fail(SA_E_NULL, "sparse_attn_route: q (or q_sums), k (or k_sums), k_scale and block_map are required");
+  if ((q && !aligned16(q)) || (k && !aligned16(k)) || (q_sums && !aligned16(q_sums)) || (k_sums && !aligned16(k_sums)))
+    return fail(SA_E_ALIGN, "sparse_attn_route: q, k, q_sums and k_sums must be 16-byte aligned");
   const int G = p->centroids_per_block;
   const bool sol = explicit_map == nullptr;
   if (sol) {
@@ -304,6 +310,7 @@ int32_t route_impl(const int8_t* q, const int8_t* k, const float* k_scale, const
   a.rule = p->rule == SA_RULE_TOPK ? sa::kRuleTopK : sa::kRuleThreshold; a.sparsity = p->sparsity;
   a.explicit_map = explicit_map; a.map = block_map; a.kc = k_centroid; a.vc = v_centroid; a.cnt = count;
   a.stats = row_stats;
+  a.q_sums = q_sums; a.k_sums = k_sums;
   if (sol) {
     char* ws = static_cast<char*>(workspace);
     const size_t qbytes = ((size_t)a.B * a.H * a.nQB * 2 * a.d + 255) & ~(size_t)255;
@@ -318,21 +325,22 @@ int32_t route_impl(const int8_t* q, const int8_t* k, const float* k_scale, const
 extern "C" {
 
 int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale, const void* v, int32_t v_dtype,
-                          const float* v_scale, const int32_t* v_block_src, const sa_dims* dims,
-                          const sa_route_params* p, const uint8_t* explicit_map, uint8_t* block_map,
-                          float* k_centroid, float* v_centroid, float* count, double* row_stats, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  return route_impl(q, k, k_scale, v, v_dtype, v_scale, v_block_src, dims, p, explicit_map, block_map, k_centroid,
-                    v_centroid, count, row_stats, workspace, workspace_bytes, false, stream);
+                          const float* v_scale, const int32_t* v_block_src, const int16_t* q_sums,
+                          const int16_t* k_sums, const sa_dims* dims, const sa_route_params* p,
+                          const uint8_t* explicit_map, uint8_t* block_map, float* k_centroid, float* v_centroid,
+                          float* count, double* row_stats, void* workspace, size_t workspace_bytes, void* stream) {
+  return route_impl(q, k, k_scale, v, v_dtype, v_scale, v_block_src, q_sums, k_sums, dims, p, explicit_map,
+                    block_map, k_centroid, v_centroid, count, row_stats, workspace, workspace_bytes, false, stream);
 }
 
 int32_t sparse_attn_route_noalloc(const int8_t* q, const int8_t* k, const float* k_scale, const void* v,
                                   int32_t v_dtype, const float* v_scale, const int32_t* v_block_src,
-                                  const sa_dims* dims, const sa_route_params* p, const uint8_t* explicit_map,
-                                  uint8_t* block_map, float* k_centroid, float* v_centroid, float* count,
-                                  double* row_stats, void* stream) {
-  return route_impl(q, k, k_scale, v, v_dtype, v_scale, v_block_src, dims, p, explicit_map, block_map, k_centroid,
-                    v_centroid, count, row_stats, nullptr, 0, true, stream);
+                                  const int16_t* q_sums, const int16_t* k_sums, const sa_dims* dims,
+                                  const sa_route_params* p, const uint8_t* explicit_map, uint8_t* block_map,
+                                  float* k_centroid, float* v_centroid, float* count, double* row_stats,
+                                  void* stream) {
+  return route_impl(q, k, k_scale, v, v_dtype, v_scale, v_block_src, q_sums, k_sums, dims, p, explicit_map,
+                    block_map, k_centroid, v_centroid, count, row_stats, nullptr, 0, true, stream);
 }
 
 int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k, const float* k_scale, const void* v,

@@ -21,13 +21,28 @@ namespace sa {
 // Source block blk is written to destination block (first + blk) mod nslots of
 // a tensor of nslots blocks: the identity for a plain quantization (first = 0,
 // nslots = L / R), a ring position for the streaming cache.
-template <int D, int R>
+//
+// With `sums` (plain quantization only) the kernel also writes the column sums
+// of the codes it has just produced over each chunk of SR rows (32 or R), int16
+// [B,H,L/SR,d] (|sum| <= 127 * 128): the routing pass then needs neither the
+// codes nor a second read of them.  Thread t holds 8 channels (one 16-byte
+// vector) of rows t / VPR + (256 / VPR) * i; the threads holding the same
+// channels meet through lane swaps inside a wave and LDS across the four
+// waves.
+template <int D, int R, int SR>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t sB,
                                                        int64_t sH, int64_t sL, int H, int valid_len,
                                                        int nslots, int first, int8_t* __restrict__ q,
-                                                       float* __restrict__ scale) {
+                                                       float* __restrict__ scale, int16_t* __restrict__ sums) {
   constexpr int VPR = D / 8;            // 16-byte vectors per row
   constexpr int NV = R * VPR / 256;     // vectors per thread
+  constexpr int RPI = 256 / VPR;        // rows between a thread's vectors
+  constexpr int NCH = R / SR;           // sum chunks per block
+  // A thread's rows are t / VPR + RPI * i with t / VPR < RPI; with RPI
+  // dividing SR, vector i lies in chunk i * RPI / SR for every thread.
+  static_assert(SR % RPI == 0 && R % SR == 0, "a thread's vectors must fall into fixed chunks");
+  static_assert(VPR == 8 || VPR == 16, "lane groups of 8 or 16 channel vectors");
+  constexpr int RPC = SR / RPI;         // a thread's rows per chunk
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const uint16_t* xb = x + b * sB + h * sH;
   float vals[NV][8];
@@ -50,6 +65,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     }
   }
   __shared__ float red[4];
+  __shared__ int part[4][NCH][D];   // per-wave chunk column sums
   amax = wave_max(amax);
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
@@ -58,10 +74,60 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   const int slot = (first + blk) % nslots;
   if (t == 0) scale[((int64_t)b * H + h) * nslots + slot] = amax / 127.0f;
   int8_t* qb = q + (((int64_t)b * H + h) * nslots + slot) * R * D;
+  uint64_t codes[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int v = t + 256 * i, r = v / VPR, cc = v % VPR;
-    *reinterpret_cast<uint64_t*>(qb + (int64_t)r * D + cc * 8) = quant8(vals[i], inv, valid[i]);
+    codes[i] = quant8(vals[i], inv, valid[i]);
+    *reinterpret_cast<uint64_t*>(qb + (int64_t)r * D + cc * 8) = codes[i];
+  }
+  if (sums == nullptr) return;   // uniform over the grid
+  // Per chunk, two channels per 32-bit word as 16-bit halves holding
+  // code + 128 (1..255) per row: flipping the sign bit of each byte turns a
+  // code into code + 128, and masking bytes 0, 2 (or 1, 3) of a dword gives
+  // channels (0, 2) (or (1, 3)) as 16-bit halves.  A wave adds SR / 4 <= 32
+  // rows into a half (<= 8160), so no carry crosses into the other half.
+  // pk[2w + s]: dword w of the vector, channels 4w + s and 4w + s + 2.
+  const int lane = t & 63, wave = t >> 6, cc = t % VPR;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    uint32_t pk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = c * RPC; i < (c + 1) * RPC; ++i) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t u = (uint32_t)(codes[i] >> (32 * w)) ^ 0x80808080u;
+        pk[2 * w] += u & 0x00FF00FFu;
+        pk[2 * w + 1] += (u >> 8) & 0x00FF00FFu;
+      }
+    }
+    // threads with the same channels inside the wave: lanes cc + VPR * k.
+    // Lane pairs (l, l ^ 16) and (l, l ^ 32) meet through the permlane swaps
+    // (VALU, no LDS traffic).
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (VPR <= 8) pk[e] += (uint32_t)__shfl_xor((int)pk[e], 8, 64);
+      const auto r16 = __builtin_amdgcn_permlane16_swap(pk[e], pk[e], false, false);
+      pk[e] = r16[0] + r16[1];
+      const auto r32 = __builtin_amdgcn_permlane32_swap(pk[e], pk[e], false, false);
+      pk[e] = r32[0] + r32[1];
+    }
+    // rows of this chunk summed into pk by the wave: (64 / VPR) lanes x RPC each
+    constexpr int bias = 128 * (64 / VPR) * RPC;
+    if (lane < VPR) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ch = cc * 8 + 4 * (e / 2) + (e % 2);
+        part[wave][c][ch] = (int)(pk[e] & 0xFFFFu) - bias;
+        part[wave][c][ch + 2] = (int)(pk[e] >> 16) - bias;
+      }
+    }
+  }
+  __syncthreads();
+  int16_t* sb = sums + (((int64_t)b * H + h) * (nslots * R / SR) + (int64_t)blk * NCH) * D;
+  for (int u = t; u < NCH * D; u += 256) {
+    const int c = u / D, ch = u % D;
+    sb[c * D + ch] = (int16_t)(part[0][c][ch] + part[1][c][ch] + part[2][c][ch] + part[3][c][ch]);
   }
 }
 
@@ -130,12 +196,22 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
 template <int D>
 static hipError_t launch_quantize_d(const QuantizeArgs& a, hipStream_t st) {
   dim3 grid(a.L / a.R, a.H, a.B);
-  if (a.R == 64)
-    quantize_kernel<D, 64><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.valid_len, a.nslots, a.first, a.q,
-                                                 a.scale);
-  else
-    quantize_kernel<D, 128><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.valid_len, a.nslots, a.first, a.q,
-                                                  a.scale);
+  // sum_rows is 32 or R (only read when sums are written)
+  if (a.R == 64) {
+    if (a.sum_rows == 64)
+      quantize_kernel<D, 64, 64><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.valid_len, a.nslots, a.first,
+                                                       a.q, a.scale, a.sums);
+    else
+      quantize_kernel<D, 64, 32><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.valid_len, a.nslots, a.first,
+                                                       a.q, a.scale, a.sums);
+  } else {
+    if (a.sum_rows == 128)
+      quantize_kernel<D, 128, 128><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.valid_len, a.nslots, a.first,
+                                                         a.q, a.scale, a.sums);
+    else
+      quantize_kernel<D, 128, 32><<<grid, 256, 0, st>>>(a.x, a.sB, a.sH, a.sL, a.H, a.valid_len, a.nslots, a.first,
+                                                        a.q, a.scale, a.sums);
+  }
   return hipGetLastError();
 }
 

@@ -8,11 +8,13 @@
 // token prefix stays exact.  FlashVSR Sparge Attention, "How it works": an
 // explicit map on logical blocks is converted to the physical block size.
 //
-// Three kernels, all reading their inputs once from HBM:
-//   pool_q   — int32 column sums of the INT8 codes of each 128-row query block
-//   pool_kv  — int32 column sums of each key block (into the workspace, for the
-//              proxy) and per-group centroids: kbar = mean of the dequantized
-//              keys, vbar = mean of V, count = valid rows
+// Two launches, reading their inputs once from HBM:
+//   pool     — int32 column sums of the INT8 codes of each 128-row query block
+//              and of each key block (into the workspace, for the proxy; taken
+//              from the quantizer's 32-row chunk sums when the caller passes
+//              them, so the codes are not read again) and per-group centroids:
+//              kbar = mean of the dequantized keys, vbar = mean of V, count =
+//              valid rows
 //   decide   — proxy s_ij = (Qsum_i . Ksum_j) * b_j / n_j (exact integer dot on
 //              the int8 matrix cores, combined in float64), then the threshold
 //              rule (mean and population std over the candidates in float64),
@@ -62,19 +64,26 @@ __device__ __forceinline__ void store_digits(int8_t* dst, int d, int col, int32_
   dst[d + col] = (int8_t)(x - 128 * hi);
 }
 
-// One workgroup per (query block, head, batch).
+// Query block i: the column sums of its codes over the valid rows, stored as
+// two int8 digits.  From the quantizer's 128-row block sums when the caller
+// passes them (padding rows are coded 0, so they add nothing), else from the
+// codes: a lane owns one dword column (4 codes) and every RG-th row.
 template <int D>
-__global__ __launch_bounds__(256) void pool_q_kernel(const int8_t* __restrict__ q, int H, int Lq,
-                                                     int lq_valid, int nQB, int8_t* __restrict__ qdig) {
+__device__ __forceinline__ void pool_q_block(const RouteArgs& a, int i, int h, int b) {
   constexpr int DW = D / 4;              // dwords per row
   constexpr int RG = 256 / DW;           // row groups
   constexpr int NR = kQBlock / RG;       // rows per lane
   __shared__ int32_t part[RG][D];
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int t = threadIdx.x;
+  const int64_t bh = (int64_t)b * a.H + h;
+  int8_t* dst = a.qdig + (bh * a.nQB + i) * 2 * D;
+  if (a.q_sums) {
+    for (int col = t; col < D; col += 256) store_digits(dst, D, col, a.q_sums[(bh * a.nQB + i) * D + col]);
+    return;
+  }
   const int dw = t % DW, rg = t / DW;
-  const int64_t bh = (int64_t)b * H + h;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(q + (bh * Lq + (int64_t)i * kQBlock) * D) + dw;
-  const int nvalid = min(kQBlock, max(0, lq_valid - i * kQBlock));
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(a.q + (bh * a.Lq + (int64_t)i * kQBlock) * D) + dw;
+  const int nvalid = min(kQBlock, max(0, a.lq_valid - i * kQBlock));
   uint32_t w[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) w[k] = src[(rg + RG * k) * DW];
@@ -87,28 +96,45 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const int8_t* __restrict__ 
     int32_t s = 0;
 #pragma unroll
     for (int r = 0; r < RG; ++r) s += part[r][col];
-    store_digits(qdig + (bh * nQB + i) * 2 * D, D, col, s);
+    store_digits(dst, D, col, s);
   }
 }
 
-// One workgroup per (key block, head, batch).  Sums are kept per 32-row chunk
-// so that 2x32 groups, and groups that span two K scale blocks, combine their
-// chunks with the right scale.
-template <int D, bool VI8, int MAXCH>
-__global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
+// The pooling pass, one launch.  Workgroup x < nKB: key block x of (head y,
+// batch z) — its column sums (into the workspace, for the proxy; per 32-row
+// chunk so that 2x32 groups, and groups spanning two K scale blocks, combine
+// their chunks with the right scale) and its centroids: kbar = mean of the
+// dequantized keys, vbar = mean of V, count = valid rows.  Workgroup x >= nKB
+// (routing rules only): query block x - nKB (pool_q_block).  With SUMS the key
+// sums come from the quantizer's chunk sums and the K codes are not read.
+template <int D, bool VI8, int MAXCH, bool SUMS>
+__global__ __launch_bounds__(256) void pool_kernel(RouteArgs a) {
   // MAXCH: 32-row chunks per key block (kblock / 32)
   constexpr int KDW = D / 4, KRG = 256 / KDW;   // K: dwords per row, row groups
   constexpr int VDW = VI8 ? D / 4 : D / 2, VRG = 256 / VDW;
   static_assert(32 % KRG == 0 && 32 % VRG == 0, "row groups must divide a chunk");
-  __shared__ int32_t kpart[KRG][MAXCH][D];
+  if ((int)blockIdx.x >= a.nKB) {                 // uniform over the workgroup
+    pool_q_block<D>(a, blockIdx.x - a.nKB, blockIdx.y, blockIdx.z);
+    return;
+  }
+  __shared__ int32_t kpart[SUMS ? 1 : KRG][MAXCH][D];
   __shared__ float vpart[VRG][MAXCH][D];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int64_t bh = (int64_t)b * a.H + h;
   const int kb = MAXCH * 32, row0 = j * kb, nch = MAXCH;
   const int nKS = a.Lkv / a.k_scale_rows;
   const int nvalid = a.lay.block_rows(j);   // valid rows: a prefix of the block
-  // K: lane (dw, rg) sums rows rg, rg + KRG, ... of each chunk
-  {
+  if (SUMS) {
+    // the chunk sums, 8 columns per lane
+    for (int u = t; u < MAXCH * D / 8; u += 256) {
+      const int c = u / (D / 8), col0 = (u % (D / 8)) * 8;
+      const v8s sv =
+          *reinterpret_cast<const v8s*>(a.k_sums + (bh * (a.Lkv / 32) + (int64_t)j * MAXCH + c) * D + col0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kpart[0][c][col0 + e] = sv[e];
+    }
+  } else {
+    // K: lane (dw, rg) sums rows rg, rg + KRG, ... of each chunk
     constexpr int NR = 32 / KRG;
     const int dw = t % KDW, rg = t / KDW;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(a.k + (bh * a.Lkv + row0) * D) + dw;
@@ -122,7 +148,7 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
       I8Cols acc;
 #pragma unroll
       for (int k = 0; k < NR; ++k) acc.add(w[c][k], c * 32 + rg + KRG * k < nvalid);
-      *reinterpret_cast<int4*>(&kpart[rg][c][dw * 4]) = acc.sums();
+      *reinterpret_cast<int4*>(&kpart[SUMS ? 0 : rg][c][dw * 4]) = acc.sums();
     }
   }
   // V (centroids only): physical rows through v_block_src, one 64-row block at a time
@@ -168,15 +194,17 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(RouteArgs a) {
   // written by the same thread only)
   for (int w = t; w < nch * D; w += 256) {
     const int c = w / D, col = w % D;
-    int32_t s = 0;
+    if (!SUMS) {
+      int32_t s = 0;
 #pragma unroll
-    for (int r = 0; r < KRG; ++r) s += kpart[r][c][col];
+      for (int r = 0; r < KRG; ++r) s += kpart[SUMS ? 0 : r][c][col];
+      kpart[0][c][col] = s;
+    }
     float vsum = 0.0f;
     if (a.G > 0) {
 #pragma unroll
       for (int r = 0; r < VRG; ++r) vsum += vpart[r][c][col];
     }
-    kpart[0][c][col] = s;
     vpart[0][c][col] = vsum;
   }
   __syncthreads();
@@ -899,17 +927,20 @@ size_t route_workspace_bytes(int B, int H, int nQB, int nKB, int d) {
 template <int D>
 static hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
   const bool sol = a.explicit_map == nullptr;
-  if (sol) {
-    pool_q_kernel<D><<<dim3(a.nQB, a.H, a.B), 256, 0, st>>>(a.q, a.H, a.Lq, a.lq_valid, a.nQB, a.qdig);
-  }
   if (sol || a.G > 0) {
-    const dim3 grid(a.nKB, a.H, a.B);
+    // key blocks, then (routing rules) query blocks
+    const dim3 grid(a.nKB + (sol ? a.nQB : 0), a.H, a.B);
+    const bool sums = a.k_sums != nullptr;
     if (a.kblock == 64) {
-      if (a.v_int8) pool_kv_kernel<D, true, 2><<<grid, 256, 0, st>>>(a);
-      else pool_kv_kernel<D, false, 2><<<grid, 256, 0, st>>>(a);
+      if (a.v_int8) sums ? pool_kernel<D, true, 2, true><<<grid, 256, 0, st>>>(a)
+                         : pool_kernel<D, true, 2, false><<<grid, 256, 0, st>>>(a);
+      else sums ? pool_kernel<D, false, 2, true><<<grid, 256, 0, st>>>(a)
+                : pool_kernel<D, false, 2, false><<<grid, 256, 0, st>>>(a);
     } else {
-      if (a.v_int8) pool_kv_kernel<D, true, 4><<<grid, 256, 0, st>>>(a);
-      else pool_kv_kernel<D, false, 4><<<grid, 256, 0, st>>>(a);
+      if (a.v_int8) sums ? pool_kernel<D, true, 4, true><<<grid, 256, 0, st>>>(a)
+                         : pool_kernel<D, true, 4, false><<<grid, 256, 0, st>>>(a);
+      else sums ? pool_kernel<D, false, 4, true><<<grid, 256, 0, st>>>(a)
+                : pool_kernel<D, false, 4, false><<<grid, 256, 0, st>>>(a);
     }
   }
   if (sol) {

@@ -12,6 +12,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef unsigned short v8us __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
 
 #define SA_LDS __attribute__((address_space(3)))
 

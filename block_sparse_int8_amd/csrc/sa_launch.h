@@ -56,6 +56,8 @@ struct QuantizeArgs {
   int8_t* q;
   float* scale;
   int nslots, first;   // destination: block b goes to slot (first + b) % nslots of q / scale
+  int16_t* sums;       // optional column sums of the codes per sum_rows chunk [B,H,L/sum_rows,d] (plain quantization)
+  int sum_rows;        // 32 or R
 };
 
 struct GatherArgs {
@@ -91,6 +93,8 @@ struct RouteArgs {
   double* stats;
   int8_t* qdig;    // workspace [B,H,nQB][2][d]: query-block column sums as two int8 digits (Sol rule only)
   int8_t* kdig;    // workspace [B,H,nKB][2][d]: key-block column sums, same form (Sol rule only)
+  const int16_t* q_sums;   // optional: the quantizer's column sums of Q per 128-row block [B,H,Lq/128,d]
+  const int16_t* k_sums;   // optional: the same for K per 32-row chunk [B,H,Lkv/32,d]
 };
 
 struct FwdArgs {

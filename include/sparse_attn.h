@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 6
+#define SA_ABI_VERSION 7
 
 enum sa_status {
   SA_OK = 0,
@@ -156,10 +156,16 @@ int32_t sa_device_check(int32_t device);
  *   x_q      out int8 [B,H,L,d] dense
  *   scale    out fp32 [B,H,L/rows_per_block]: amax/127 of the block (0 if all
  *            zero); code = clamp(round-half-even(x * (127/amax)), -127, 127)
+ *   col_sums optional out int16 [B,H,L/sum_rows,d] (NULL: not written): the
+ *            column sums of the written codes over each chunk of sum_rows
+ *            rows (32, or rows_per_block; ignored when col_sums is NULL).
+ *            Handed to sparse_attn_route as q_sums (Q, sum_rows 128) and k_sums
+ *            (K, sum_rows 32) they spare the route a second read of the codes.
  * Bit-exact with a plain IEEE float32 evaluation of that rule. */
 int32_t quantize_qk_int8(const void* x_bf16, int64_t sB, int64_t sH, int64_t sL, int32_t B,
                          int32_t H, int32_t L, int32_t d, int32_t valid_len,
-                         int32_t rows_per_block, int8_t* x_q, float* scale, void* stream);
+                         int32_t rows_per_block, int8_t* x_q, float* scale, int16_t* col_sums,
+                         int32_t sum_rows, void* stream);
 
 /* Streaming INT8 K/V cache append (FlashVSR Kitchen Sparse Attention, opening
  * section: in streaming use each block holds the recent K/V history as INT8,
@@ -192,6 +198,14 @@ size_t sparse_attn_route_workspace_size(const sa_dims* dims, const sa_route_para
  * logical blocks converted to the physical key-block size).
  *   q         int8 [B,H,Lq,d] (quantized with 128-row blocks)
  *   k         int8 [B,H,Lkv,d], k_scale fp32 [B,H,Lkv/k_scale_rows]
+ *   q_sums, k_sums  optional int16 [B,H,Lq/128,d] and [B,H,Lkv/32,d]: the
+ *             col_sums quantize_qk_int8 wrote with q (sum_rows 128) and k
+ *             (sum_rows 32).  When given, the
+ *             block sums come from them and q (resp. k) is not read and may be
+ *             NULL.  They count every row of a chunk, which equals the sum over
+ *             the valid rows because padding rows are coded 0 (past the valid
+ *             length always; inside a segmented layout when they hold zeros, as
+ *             required above).
  *   v         [B,H,Lv,d] bf16 (v_dtype SA_BF16) or int8 (SA_INT8, with v_scale
  *             fp32 [B,H,Lv/v_scale_rows]); logical key row r reads V row
  *             v_block_src[r/64]*64 + r%64 when v_block_src (int32 [Lkv/64]) is
@@ -228,6 +242,7 @@ size_t sparse_attn_route_workspace_size(const sa_dims* dims, const sa_route_para
  * SA_RULE_TOPK decisions are bit-exact. */
 int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale, const void* v,
                           int32_t v_dtype, const float* v_scale, const int32_t* v_block_src,
+                          const int16_t* q_sums, const int16_t* k_sums,
                           const sa_dims* dims, const sa_route_params* p,
                           const uint8_t* explicit_map, uint8_t* block_map, float* k_centroid,
                           float* v_centroid, float* count, double* row_stats, void* workspace,
@@ -250,6 +265,7 @@ int32_t sparse_attn_route(const int8_t* q, const int8_t* k, const float* k_scale
  * The array keeps the last call's contents, which no later call reads. */
 int32_t sparse_attn_route_noalloc(const int8_t* q, const int8_t* k, const float* k_scale, const void* v,
                                   int32_t v_dtype, const float* v_scale, const int32_t* v_block_src,
+                                  const int16_t* q_sums, const int16_t* k_sums,
                                   const sa_dims* dims, const sa_route_params* p,
                                   const uint8_t* explicit_map, uint8_t* block_map, float* k_centroid,
                                   float* v_centroid, float* count, double* row_stats, void* stream);

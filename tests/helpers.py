@@ -28,8 +28,11 @@ def bf16_dev(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def gpu_pipeline(wl, tau=None, out_dtype=torch.float32, kblock=None, map_kblock=None, G=None):
-    """The whole HIP path for one workload.  Returns host numpy arrays."""
+def gpu_pipeline(wl, tau=None, out_dtype=torch.float32, kblock=None, map_kblock=None, G=None, sums=True):
+    """The whole HIP path for one workload.  Returns host numpy arrays.
+    ``sums``: the quantizer also writes the codes' column sums and the route
+    takes them (as bench.py and sparse_attention run it); False: the route
+    sums the codes itself."""
     import block_sparse_int8_amd as sa
     tau = wl.threshold if tau is None else tau
     kblock = wl.kblock if kblock is None else kblock
@@ -37,13 +40,19 @@ def gpu_pipeline(wl, tau=None, out_dtype=torch.float32, kblock=None, map_kblock=
     q = bf16_dev(wl.q)
     k = bf16_dev(wl.k)
     v = bf16_dev(wl.v)
-    q8, qs = sa.quantize_qk_int8(q, wl.lq_valid, 128)
+    qsum = ksum = None
+    if sums:
+        q8, qs, qsum = sa.quantize_qk_int8(q, wl.lq_valid, 128, col_sums=True, sum_rows=128)
+    else:
+        q8, qs = sa.quantize_qk_int8(q, wl.lq_valid, 128)
     vbs = None
     if wl.virtual:
         cos = torch.from_numpy(wl.rope_cos).cuda()
         sin = torch.from_numpy(wl.rope_sin).cuda()
         k8, ks, vbs = sa.gather_virtual_kv(k, wl.rows_per_slice, wl.src_map.tolist(), cos, sin, wl.rot_offset,
                                            wl.k_scale_rows)
+    elif sums:
+        k8, ks, ksum = sa.quantize_qk_int8(k, wl.lkv_valid, wl.k_scale_rows, col_sums=True, sum_rows=32)
     else:
         k8, ks = sa.quantize_qk_int8(k, wl.lkv_valid, wl.k_scale_rows)
     v_in, vsc = v, None
@@ -58,7 +67,7 @@ def gpu_pipeline(wl, tau=None, out_dtype=torch.float32, kblock=None, map_kblock=
                              prefix_tokens=wl.prefix_tokens, kblock=kblock, k_scale_rows=wl.k_scale_rows,
                              v_scale_rows=wl.v_scale_rows, explicit_map=em,
                              map_kblock=map_kblock or wl.map_kblock, rule=wl.rule, sparsity=wl.sparsity,
-                             segments=wl.segments, row_stats=True)
+                             segments=wl.segments, row_stats=True, q_sums=qsum, k_sums=ksum)
     if wl.qk_float:
         out, lse = sa.sparse_attn_fwd_float(q, k, v, r["map"], k_centroid=r["k_centroid"],
                                             v_centroid=r["v_centroid"], count=r["count"], lq_valid=wl.lq_valid,
@@ -80,6 +89,7 @@ def gpu_pipeline(wl, tau=None, out_dtype=torch.float32, kblock=None, map_kblock=
                v_block_src=host(vbs))
     if wl.v_int8:
         res["v8"], res["v_scale"] = host(v_in), host(vsc)
+    res["q_sums"], res["k_sums"] = host(qsum), host(ksum)
     return res
 
 

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 6
+    assert sa.load().sa_abi_version() == sa.ABI_VERSION == 7
 
 
 def test_missing_library_lists_search_paths(monkeypatch, tmp_path):
@@ -73,14 +73,14 @@ def _err():
 def test_quantize_validation_before_any_device_call():
     lib = _lib()
     p = ctypes.c_void_p(16)     # never dereferenced: validation fails first
-    assert lib.quantize_qk_int8(None, 0, 0, 0, 1, 1, 128, 128, 128, 128, p, p, None) == sa.SA_E_NULL
-    assert lib.quantize_qk_int8(p, 0, 0, 128, 1, 1, 128, 96, 128, 128, p, p, None) == sa.SA_E_SHAPE
+    assert lib.quantize_qk_int8(None, 0, 0, 0, 1, 1, 128, 128, 128, 128, p, p, None, 32, None) == sa.SA_E_NULL
+    assert lib.quantize_qk_int8(p, 0, 0, 128, 1, 1, 128, 96, 128, 128, p, p, None, 32, None) == sa.SA_E_SHAPE
     assert "d must be" in _err()
-    assert lib.quantize_qk_int8(p, 0, 0, 128, 1, 1, 128, 128, 128, 32, p, p, None) == sa.SA_E_VALUE
-    assert lib.quantize_qk_int8(p, 0, 0, 128, 1, 1, 100, 128, 100, 64, p, p, None) == sa.SA_E_SHAPE
-    assert lib.quantize_qk_int8(p, 0, 0, 128, 1, 1, 128, 128, 129, 64, p, p, None) == sa.SA_E_SHAPE
-    assert lib.quantize_qk_int8(ctypes.c_void_p(8), 0, 0, 128, 1, 1, 128, 128, 128, 64, p, p, None) == sa.SA_E_ALIGN
-    assert lib.quantize_qk_int8(p, 0, 0, 100, 1, 1, 128, 128, 128, 64, p, p, None) == sa.SA_E_ALIGN
+    assert lib.quantize_qk_int8(p, 0, 0, 128, 1, 1, 128, 128, 128, 32, p, p, None, 32, None) == sa.SA_E_VALUE
+    assert lib.quantize_qk_int8(p, 0, 0, 128, 1, 1, 100, 128, 100, 64, p, p, None, 32, None) == sa.SA_E_SHAPE
+    assert lib.quantize_qk_int8(p, 0, 0, 128, 1, 1, 128, 128, 129, 64, p, p, None, 32, None) == sa.SA_E_SHAPE
+    assert lib.quantize_qk_int8(ctypes.c_void_p(8), 0, 0, 128, 1, 1, 128, 128, 128, 64, p, p, None, 32, None) == sa.SA_E_ALIGN
+    assert lib.quantize_qk_int8(p, 0, 0, 100, 1, 1, 128, 128, 128, 64, p, p, None, 32, None) == sa.SA_E_ALIGN
 
 
 def _dims(**kw):
@@ -102,7 +102,8 @@ def _route(dims, prm, em=None, ws=None, wsb=0, G_out=True):
     lib = _lib()
     p = ctypes.c_void_p(256)
     c = p if G_out else None
-    return lib.sparse_attn_route(p, p, p, p, sa.SA_BF16, None, None, ctypes.byref(dims), ctypes.byref(prm), em, p,
+    return lib.sparse_attn_route(p, p, p, p, sa.SA_BF16, None, None, None, None, ctypes.byref(dims), ctypes.byref(prm),
+                                 em, p,
                                  c, c, c, None, ws, wsb, None)
 
 

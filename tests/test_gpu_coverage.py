@@ -223,3 +223,99 @@ def test_row_stats_and_partial_block_proxies(sa, orc):
         g = gpu_pipeline(wl)
         o = orc.run(wl)
         assert np.array_equal(g["map"], o["map"]), sp
+
+
+# ---------------------------------------------------------------------------
+# Column sums from the quantizer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,R,SR,L,valid", [(128, 64, 32, 1024, 1000), (128, 64, 64, 1024, 1000),
+                                            (128, 128, 128, 1024, 1000), (128, 128, 32, 1024, 1000),
+                                            (64, 64, 32, 512, 300), (64, 128, 128, 512, 512),
+                                            (64, 128, 32, 512, 77), (128, 128, 128, 256, 0)])
+def test_quantize_column_sums(sa, orc, d, R, SR, L, valid):
+    """The quantizer's optional column sums equal the sums of the oracle's codes
+    over every chunk of SR rows (padding rows coded 0), and the codes are the
+    same whether or not the sums are written."""
+    say(f"case col sums d={d} R={R} SR={SR} L={L} valid={valid}")
+    rng = np.random.default_rng(d + R + L + valid + SR)
+    x = rng.standard_normal((2, 3, L, d), dtype=np.float32) * rng.uniform(0.1, 10, (2, 3, 1, 1)).astype(np.float32)
+    if L >= 2 * R:
+        # a block of codes +-127 with one sign per column: sums reach +-127 * SR
+        x[1, 1, :R] = np.float32(127.0 / 64) * np.sign(rng.standard_normal(d)).astype(np.float32)[None, :]
+    xb = bf16_bits(x)
+    g8, gs, gsum = sa.quantize_qk_int8(bf16_dev(xb), valid, R, col_sums=True, sum_rows=SR)
+    o8, os_ = orc.quantize(xb, valid, R)
+    assert np.array_equal(g8.cpu().numpy(), o8) and np.array_equal(gs.cpu().numpy(), os_)
+    ref = o8.astype(np.int64).reshape(2, 3, L // SR, SR, d).sum(axis=3)
+    assert gsum.dtype == torch.int16 and np.array_equal(gsum.cpu().numpy().astype(np.int64), ref)
+    # a strided view ([B,L,H,d] memory)
+    blhd = bf16_dev(np.ascontiguousarray(xb.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+    _, _, gsum2 = sa.quantize_qk_int8(blhd, valid, R, col_sums=True, sum_rows=SR)
+    assert np.array_equal(gsum2.cpu().numpy(), gsum.cpu().numpy())
+
+
+def _sums_cases():
+    c3 = W.config(3, small=True)
+    c4 = W.config(4, small=True)
+    k128 = W.tiny_sol(seed=90, H=2, L=1024, d=128, valid=1000, centroids_per_block=2)
+    k128.kblock = k128.k_scale_rows = 128
+    topk = W.config(3, small=True)
+    topk.rule, topk.sparsity = 1, 0.75
+    seg = W.ref2va_segments(H=2, text=77, ref_image=300, ref_audio=40, ref_video_frames=1, video_frames=2,
+                            frame_tokens=320, centroids_per_block=2)
+    cache = W.tiny_sol(seed=91, H=2, L=1024, d=128, valid=1000, centroids_per_block=2)
+    cache.kblock, cache.k_scale_rows, cache.map_kblock = 128, 64, 128
+    cache.v_int8, cache.v_scale_rows = True, 128
+    cache.explicit_map = np.random.default_rng(92).choice(np.array([EXACT, CENTROID, DROP], np.uint8),
+                                                          size=(1, 2, 8, 8), p=[0.45, 0.45, 0.1])
+    d64 = W.tiny_sol(seed=93, H=3, L=640, d=64, valid=577, centroids_per_block=1)
+    return {"tiny": W.config(1), "wan_small": c3, "prefix_2x32": c4, "kblock128": k128, "topk": topk,
+            "segments": seg, "int8_cache_explicit": cache, "d64": d64}
+
+
+@pytest.mark.parametrize("name", list(_sums_cases().keys()))
+def test_route_from_sums_equals_route_from_codes(sa, name):
+    """The route fed the quantizer's column sums gives the same map, centroids,
+    counts and statistics, and the forward the same output, as the route that
+    sums the codes itself, bit for bit."""
+    wl = _sums_cases()[name]
+    say(f"case sums vs codes {name}")
+    a = gpu_pipeline(wl, sums=True)
+    b = gpu_pipeline(wl, sums=False)
+    assert a["k_sums"] is not None
+    for key in ("map", "kbar", "vbar", "count", "stats", "out", "lse"):
+        if a[key] is None:
+            continue
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def test_route_reads_no_codes_when_given_sums(sa):
+    """Through the C ABI: with q_sums and k_sums the route accepts NULL q and k
+    and gives the binding's result."""
+    import ctypes
+    wl = W.config(3, small=True)
+    q8, qs, qsum = sa.quantize_qk_int8(bf16_dev(wl.q), wl.lq_valid, 128, col_sums=True, sum_rows=128)
+    k8, ks, ksum = sa.quantize_qk_int8(bf16_dev(wl.k), wl.lkv_valid, 64, col_sums=True, sum_rows=32)
+    v = bf16_dev(wl.v)
+    ref = sa.sparse_attn_route(q8, k8, ks, v, lq_valid=wl.lq_valid, lkv_valid=wl.lkv_valid, threshold=1.0,
+                               centroids_per_block=1, row_stats=True)
+    B, H, Lq, d = q8.shape
+    nQB, nKB = Lq // 128, wl.Lkv // 64
+    dims = sa.sa_dims(B, H, Lq, wl.Lkv, d, wl.lq_valid, wl.lkv_valid, wl.Lkv)
+    prm = sa._params(1.0, 1, 0, 64, 64, 128, 64)
+    lib = sa.load()
+    ws_bytes = lib.sparse_attn_route_workspace_size(ctypes.byref(dims), ctypes.byref(prm), 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    bmap = torch.empty((B, H, nQB, nKB), dtype=torch.uint8, device="cuda")
+    kc = torch.empty((B, H, nKB, 1, d), dtype=torch.float32, device="cuda")
+    vc, cnt = torch.empty_like(kc), torch.empty((B, H, nKB, 1), dtype=torch.float32, device="cuda")
+    st = torch.empty((B, H, nQB, 2), dtype=torch.float64, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = lib.sparse_attn_route(None, None, P(ks), P(v), sa.SA_BF16, None, None, P(qsum), P(ksum), ctypes.byref(dims),
+                               ctypes.byref(prm), None, P(bmap), P(kc), P(vc), P(cnt), P(st), P(ws), ws_bytes,
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, lib.sa_last_error()
+    torch.cuda.synchronize()
+    for got, key in ((bmap, "map"), (kc, "k_centroid"), (vc, "v_centroid"), (cnt, "count"), (st, "row_stats")):
+        assert torch.equal(got, ref[key]), key

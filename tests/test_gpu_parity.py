@@ -22,9 +22,10 @@ def sa():
     return m
 
 
-def _check_workload(orc, wl, tau=None, sel=None, out_dtype=torch.float32, tol=(MAX_ABS, MEAN_ABS)):
-    say(f"case {wl.name} H={wl.H} Lq={wl.Lq} Lkv={wl.Lkv} d={wl.d} tau={tau if tau is not None else wl.threshold}")
-    g = gpu_pipeline(wl, tau=tau, out_dtype=out_dtype)
+def _check_workload(orc, wl, tau=None, sel=None, out_dtype=torch.float32, tol=(MAX_ABS, MEAN_ABS), sums=True):
+    say(f"case {wl.name} H={wl.H} Lq={wl.Lq} Lkv={wl.Lkv} d={wl.d} tau={tau if tau is not None else wl.threshold} "
+        f"sums={sums}")
+    g = gpu_pipeline(wl, tau=tau, out_dtype=out_dtype, sums=sums)
     o = orc.run(wl, sel=sel, tau=tau)
     assert np.array_equal(g["q8"], o["q8"]) and np.array_equal(g["q_scale"], o["q_scale"]), "Q codes differ"
     assert np.array_equal(g["k8"], o["k8"]) and np.array_equal(g["k_scale"], o["k_scale"]), "K codes differ"

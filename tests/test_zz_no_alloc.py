@@ -70,8 +70,8 @@ def test_noalloc_refuses_shapes_beyond_the_array():
     prm = sa._params(1.0, 1, 0, 64, 64, 128, 64)
     assert lib.sparse_attn_route_workspace_size(ctypes.byref(dims), ctypes.byref(prm), 0) > 16 << 20
     fake = ctypes.c_void_p(1 << 20)         # never dereferenced: validation fails first
-    rc = lib.sparse_attn_route_noalloc(fake, fake, fake, fake, sa.SA_BF16, None, None, ctypes.byref(dims),
-                                       ctypes.byref(prm), None, fake, fake, fake, fake, None, None)
+    rc = lib.sparse_attn_route_noalloc(fake, fake, fake, fake, sa.SA_BF16, None, None, None, None,
+                                       ctypes.byref(dims), ctypes.byref(prm), None, fake, fake, fake, fake, None, None)
     assert rc == sa.SA_E_WORKSPACE
     msg = lib.sa_last_error().decode()
     assert "sparse_attn_route_noalloc" in msg and str(16 << 20) in msg
