@@ -373,6 +373,8 @@ int32_t sparse_attn_fwd(const int8_t* q, const float* q_scale, const int8_t* k, 
   a.lq_valid = dims->lq_valid; a.lkv_valid = dims->lkv_valid;
   a.nQB = dims->Lq / 128; a.nKB = dims->Lkv / p->kblock; a.kblock = p->kblock; a.G = p->centroids_per_block;
   a.k_scale_rows = p->k_scale_rows; a.v_scale_rows = p->v_scale_rows;
+  a.ks_shift = p->k_scale_rows == 128 ? 7 : 6;
+  a.vs_shift = v_dtype == SA_INT8 && p->v_scale_rows == 128 ? 7 : 6;
   a.v_int8 = v_dtype == SA_INT8; a.out_bf16 = out_dtype == SA_BF16;
   a.sm_log2 = sm_scale * 1.4426950408889634f;
   if ((int64_t)a.B * a.H * a.nQB > 0x7FFFFFFF) return fail(SA_E_SHAPE, "sparse_attn_fwd: too many query blocks");

@@ -229,19 +229,27 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // barrier (which waits for all of this wave's loads).
 struct TileInfo {
   int krow0;
-  int vsrc;               // V row of the tile (raw load when V rows are remapped)
+  int vblk;               // V block of the tile: raw table entry when V rows are remapped (clamped when used)
+  int nvb;                // V blocks of the tensor (clamp bound), 0 when V rows are not remapped
   float kscale, pscale;
-  __device__ __forceinline__ int vrow0() const { return __builtin_amdgcn_readfirstlane(vsrc); }
+  __device__ __forceinline__ int vrow0() const {
+    const int vb = nvb > 0 ? min(max(vblk, 0), nvb - 1) : vblk;
+    return __builtin_amdgcn_readfirstlane(vb) * kTile;
+  }
 };
 
+// The loads are only issued here: nothing waits for them until the tile is
+// used, an iteration later (the V table entry is clamped then too).  Scale
+// indices are shifts (k_scale_rows and v_scale_rows are 64 or 128).
 template <bool QF, bool VI8>
 __device__ __forceinline__ TileInfo fetch_tile(const FwdArgs& a, int64_t bh, int kt, int nKS, int nVS) {
   TileInfo t;
   t.krow0 = kt * kTile;
-  t.vsrc = a.v_block_src ? min(max(a.v_block_src[kt], 0), a.Lv / kTile - 1) * kTile : t.krow0;
-  if (VI8) t.vsrc = __builtin_amdgcn_readfirstlane(t.vsrc);   // the V scale index needs it now
-  t.kscale = QF ? 1.0f : a.k_scale[bh * nKS + t.krow0 / a.k_scale_rows];
-  t.pscale = VI8 ? a.v_scale[bh * nVS + t.vsrc / a.v_scale_rows] : 1.0f;
+  t.nvb = a.v_block_src ? a.Lv / kTile : 0;
+  t.vblk = a.v_block_src ? a.v_block_src[kt] : kt;
+  t.kscale = QF ? 1.0f : a.k_scale[bh * nKS + (t.krow0 >> a.ks_shift)];
+  // INT8 V needs its block's scale, which depends on the table entry
+  t.pscale = VI8 ? a.v_scale[bh * nVS + ((t.vrow0()) >> a.vs_shift)] : 1.0f;
   return t;
 }
 
@@ -757,6 +765,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       constexpr int PN = TileCopy<D, KB, VI8>::PIECES;
       TileInfo t0 = fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS);
       TileInfo t1 = nE > 1 ? fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[1]), nKS, nVS) : t0;
+      // list entry of tile T + 2, read one iteration before it is needed so
+      // the top of an iteration does not wait for an LDS read
+      int next_entry = elist[min(2, nE - 1)];
       if (VI8) load_v_int8<D>(v8base + (int64_t)t0.vrow0() * D, vr, tid);
       tile_copy<D, KB, VI8>(t0, t0, kst0, vst0, krs, vrs, plan, wave).all();
       tile_copy<D, KB, VI8>(t1, t1, kst1, vst1, krs, vrs, plan, wave).all_k();
@@ -781,8 +792,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         uint8_t* const vwr = ODD ? vst0 : vst1;   // V of tile T+1 goes here
         copies_done_barrier();
         const TileInfo t2 =
-            T + 2 < nE ? fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[T + 2]), nKS, nVS)
+            T + 2 < nE ? fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + next_entry), nKS, nVS)
                        : t1;
+        next_entry = elist[min(T + 3, nE - 1)];
         if (VI8) load_v_int8<D>(v8base + (int64_t)t1.vrow0() * D, vr, tid);
         const TileCopy<D, KB, VI8> cp = tile_copy<D, KB, VI8>(t2, t1, kwr, vwr, krs, vrs, plan, wave);
         pipe_step<D, QF, VI8, true, true, true, 0, PH>(krd, vrd, qf, seed, sA, sB, pA, pB, O, m_run, l_run,
@@ -1010,6 +1022,7 @@ hipError_t launch_fwd_float(const FwdFloatArgs& f, hipStream_t st) {
   a.nQB = f.nQB; a.nKB = f.nKB; a.kblock = f.kblock; a.G = f.G;
   a.k_scale_rows = kTile;   // unused on this path (no K scales); kept non-zero
   a.v_scale_rows = kTile;
+  a.ks_shift = a.vs_shift = 6;
   a.lay = f.lay;
   a.v_int8 = false;
   a.out_bf16 = f.out_bf16;

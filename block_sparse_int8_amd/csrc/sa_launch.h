@@ -115,6 +115,7 @@ struct FwdArgs {
   float* lse;
   int B, H, Lq, Lkv, Lv, d, lq_valid, lkv_valid;
   int nQB, nKB, kblock, G, k_scale_rows, v_scale_rows;
+  int ks_shift, vs_shift;   // log2 of k_scale_rows and v_scale_rows
   KvLayout lay;
   bool v_int8, out_bf16;
   float sm_log2;   // sm_scale * log2(e)
