@@ -550,7 +550,7 @@ __device__ constexpr int step_index(int m) {
 // vh: the V half (32 rows) that p_prev weighs (DO_PV); s_cur: the scores
 // whose weights go to p_cur (DO_W), with their row-sum part added to l_run
 // after the fast-path check.  The copy pieces [P0, P1) of cp are issued in
-// between.
+// between, piece P0 + k in segment k.
 template <int D, bool QF, bool VI8, bool DO_QK, bool DO_PV, bool DO_W, int P0, int P1>
 __device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, const QFrag<D, QF>& qf,
                                           const SAcc<QF>& seed, SAcc<QF>& s_next, const SAcc<QF>& s_cur,
@@ -587,9 +587,10 @@ __device__ __forceinline__ void pipe_step(const uint8_t* kh, const uint8_t* vh, 
       for (int e = 0; e < 8; ++e)
         if (e * M / 8 == m) weight_pair<VI8>(s_cur, e, c, b, pscale, ps, p_cur);
     }
+    static_assert(NC <= M, "at most one copy piece per scheduling segment");
 #pragma unroll
     for (int k = 0; k < NC; ++k)
-      if ((2 * k + 1) * M / (2 * (NC > 0 ? NC : 1)) == m) cp.piece(P0 + k);
+      if (k == m) cp.piece(P0 + k);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (DO_W) {
@@ -761,7 +762,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // repeats tile T+1 into the free stage, which nothing reads.
     // Registers: scores of even halves sA, odd halves sB; weights pA / pB.
     if (nE > 0) {
-      constexpr int PH = (TileCopy<D, KB, VI8>::PIECES + 1) / 2;   // copy pieces in a tile's first step
+      // Every copy piece goes into a tile's first step, one per scheduling
+      // segment from its start: the copies then have the rest of the tile to
+      // land before the next barrier waits for them (measured faster than
+      // spreading them over both steps or issuing two per segment).
+      constexpr int PH = TileCopy<D, KB, VI8>::PIECES;   // copy pieces in a tile's first step
       constexpr int PN = TileCopy<D, KB, VI8>::PIECES;
       TileInfo t0 = fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS);
       TileInfo t1 = nE > 1 ? fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[1]), nKS, nVS) : t0;
