@@ -61,6 +61,23 @@ int32_t check_device(int dev) {
   return SA_OK;
 }
 
+// Compute units of device dev, read once per device (256 on MI355X).
+int g_cus[kMaxDev] = {0};
+
+int device_cus(int dev) {
+  if (dev < 0 || dev >= kMaxDev) return 256;
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    g_cus[dev] = n;
+  }
+  return g_cus[dev];
+}
+
 int32_t check_current_device(int* dev_out = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
@@ -311,6 +328,7 @@ int32_t route_impl(const int8_t* q, const int8_t* k, const float* k_scale, const
   a.explicit_map = explicit_map; a.map = block_map; a.kc = k_centroid; a.vc = v_centroid; a.cnt = count;
   a.stats = row_stats;
   a.q_sums = q_sums; a.k_sums = k_sums;
+  a.num_cus = device_cus(dev);
   if (sol) {
     char* ws = static_cast<char*>(workspace);
     const size_t qbytes = ((size_t)a.B * a.H * a.nQB * 2 * a.d + 255) & ~(size_t)255;

@@ -308,17 +308,17 @@ struct ProxyTiles {
   __device__ __forceinline__ int row_of(int e) const { return (e / 4) * 8 + hf * 4 + (e % 4); }
 };
 
-// Work item of a decision workgroup: (32-query-block chunk, head, batch) from a
-// 1-D grid of chunks * H * B.  Hardware workgroup id w runs on XCD w % 8; each
-// XCD is given a contiguous range of work items, so the chunks of one head,
-// which all read that head's key-block sums, share one L2.
+// Work item of a decision workgroup: (chunk of R query blocks, head, batch)
+// from a 1-D grid of chunks * H * B.  Hardware workgroup id w runs on XCD
+// w % 8; each XCD is given a contiguous range of work items, so the chunks of
+// one head, which all read that head's key-block sums, share one L2.
 struct DecideItem {
   int i0, h, b;
-  __device__ __forceinline__ DecideItem(const RouteArgs& a) {
-    const int nwg = gridDim.x, nch = (a.nQB + 31) / 32;
+  __device__ __forceinline__ DecideItem(const RouteArgs& a, int R = 32) {
+    const int nwg = gridDim.x, nch = (a.nQB + R - 1) / R;
     int w = blockIdx.x;
     if ((nwg & 7) == 0) w = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-    i0 = (w % nch) * 32;
+    i0 = (w % nch) * R;
     h = (w / nch) % a.H;
     b = w / (nch * a.H);
   }
@@ -619,17 +619,19 @@ __global__ __launch_bounds__(64 * kDecideWaves) void decide_topk_kernel(RouteArg
 
 // ---------------------------------------------------------------------------
 // Decisions with the proxies held in LDS.  When a query block has at most
-// kLdsCand candidates, one pass of matrix-core tiles writes s_ij for the 32
-// query blocks of a workgroup into a 32 x kLdsCand float64 array (128 KiB),
-// and every later pass reads it from there (slot j - jc0; NaN for slots that
-// hold no candidate).  The rules and their arithmetic are
-// those of the kernels above; only where s lives changes (and the summation
-// order of the mean and variance).  One workgroup per CU; kLdsWaves waves.
+// kLdsCand candidates, one pass of matrix-core tiles writes s_ij for the R
+// query blocks of a workgroup into an R x kLdsCand float64 array, and every
+// later pass reads it from there (slot j - jc0; NaN for slots that hold no
+// candidate).  The rules and their arithmetic are those of the kernels above;
+// only where s lives changes (and the summation order of the mean and
+// variance).  R = 32 (128 KiB, one workgroup per CU) or R = 16 (64 KiB, two
+// per CU; the 32-row proxy tiles then keep only their first 16 rows), picked
+// at launch (see launch_route_d).
 // ---------------------------------------------------------------------------
 constexpr int kLdsCand = 512;
 constexpr int kLdsWaves = 8;
 
-template <int D, int NW>
+template <int D, int NW, int R>
 __device__ __forceinline__ void proxies_to_lds(const RouteArgs& a, const ProxyTiles<D>& pt, const CandRange& cr,
                                                int wave, double (*sv_s)[kLdsCand]) {
   // at most kLdsCand / 32 + 1 column tiles, so at most MT per wave: all of a
@@ -650,11 +652,12 @@ __device__ __forceinline__ void proxies_to_lds(const RouteArgs& a, const ProxyTi
     if (j < cr.jc0 || j >= cr.jc1) continue;
     const bool cand = cr.has(j);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sv_s[pt.row_of(e)][j - cr.jc0] = cand ? sv[e] : __builtin_nan("");
+    for (int e = 0; e < 16; ++e)
+      if (R == 32 || pt.row_of(e) < R) sv_s[pt.row_of(e)][j - cr.jc0] = cand ? sv[e] : __builtin_nan("");
   }
   // slots past the candidate range hold NaN too, so later passes read every slot
   const int span = cr.jc1 - cr.jc0;
-  for (int x = threadIdx.x; x < 32 * kLdsCand; x += 64 * NW) {
+  for (int x = threadIdx.x; x < R * kLdsCand; x += 64 * NW) {
     const int r = x / kLdsCand, c = x % kLdsCand;
     if (c >= span) sv_s[r][c] = __builtin_nan("");
   }
@@ -671,10 +674,10 @@ __device__ __forceinline__ void fill_classes(const RouteArgs& a, int nt, uint8_t
 // valid rows, EXACT for dense ones, cand_state(r, j - jc0) for candidates.  A
 // thread owns groups of four consecutive key blocks of one row and writes the
 // four states with one store when the row allows it.
-template <typename F>
+template <int R, typename F>
 __device__ __forceinline__ void write_map_rows(const RouteArgs& a, int64_t bh, int i0, const CandRange& cr, int nt,
                                                const uint8_t* cls_s, F cand_state) {
-  const int ng = (a.nKB + 3) / 4, rows = min(32, a.nQB - i0);
+  const int ng = (a.nKB + 3) / 4, rows = min(R, a.nQB - i0);
   const bool wide = (a.nKB & 3) == 0 && (reinterpret_cast<uintptr_t>(a.map) & 3) == 0;   // 4-byte aligned rows
   for (int x = threadIdx.x; x < ng * rows; x += nt) {
     const int r = x / ng, j0 = (x % ng) * 4;
@@ -699,21 +702,22 @@ __device__ __forceinline__ void write_map_rows(const RouteArgs& a, int64_t bh, i
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, int R>
 __global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
-  constexpr int NT = 64 * NW, TPR = NT / 32;   // threads per query-block row
-  __shared__ double sv_s[32][kLdsCand];
-  __shared__ double thr_s[32];
-  __shared__ int keep_s[32];
+  constexpr int NT = 64 * NW, TPR = NT / R;   // threads per query-block row
+  static_assert(TPR <= 64 && (kLdsCand / TPR) % 8 == 0, "row groups inside a wave, slots in batches of 8");
+  __shared__ double sv_s[R][kLdsCand];
+  __shared__ double thr_s[R];
+  __shared__ int keep_s[R];
   __shared__ __attribute__((aligned(4))) uint8_t cls_s[kMaxRouteKB + 4];
-  const DecideItem wi(a);
+  const DecideItem wi(a, R);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t bh = (int64_t)wi.b * a.H + wi.h;
   const int i0 = wi.i0;
   const ProxyTiles<D> pt(a, bh, i0, lane);
   const CandRange cr(a);
   const int N = cr.N;
-  proxies_to_lds<D, NW>(a, pt, cr, wave, sv_s);
+  proxies_to_lds<D, NW, R>(a, pt, cr, wave, sv_s);
   fill_classes(a, NT, cls_s);
   __syncthreads();
   // row r's mean and population variance: TPR adjacent lanes per row
@@ -759,7 +763,7 @@ __global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  write_map_rows(a, bh, i0, cr, NT, cls_s, [&](int rr, int c) -> uint32_t {
+  write_map_rows<R>(a, bh, i0, cr, NT, cls_s, [&](int rr, int c) -> uint32_t {
     return 1u + ((uint32_t)(keep_s[rr] == 0) & (uint32_t)(sv_s[rr][c] > thr_s[rr]));
   });
 }
@@ -776,16 +780,16 @@ __global__ __launch_bounds__(64 * NW) void decide_sol_lds_kernel(RouteArgs a) {
 // summed over the wave with one ballot per bit of it: the scalar unit, shared
 // by the CU's waves, issues a few instructions per step.  No atomics and no
 // barriers.
-template <int D, int NW>
+template <int D, int NW, int R>
 __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int NV = kLdsCand / 64;   // candidates per lane
-  __shared__ double sv_s[32][kLdsCand];
-  __shared__ uint64_t phi_s[32];
-  __shared__ uint32_t plo_s[32];
-  __shared__ int nb_s[32];
+  __shared__ double sv_s[R][kLdsCand];
+  __shared__ uint64_t phi_s[R];
+  __shared__ uint32_t plo_s[R];
+  __shared__ int nb_s[R];
   __shared__ __attribute__((aligned(4))) uint8_t cls_s[kMaxRouteKB + 4];
-  const DecideItem wi(a);
+  const DecideItem wi(a, R);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t bh = (int64_t)wi.b * a.H + wi.h;
   const int i0 = wi.i0;
@@ -794,16 +798,16 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
   const int keep = N - (int)floor((double)a.sparsity * (double)N);
   const uint8_t pruned = a.G > 0 ? 2 : 0;
   const bool select = keep > 0 && keep < N;
-  if (t < 32 && a.stats && i0 + t < a.nQB) {
+  if (t < R && a.stats && i0 + t < a.nQB) {
     a.stats[(bh * a.nQB + i0 + t) * 2] = __builtin_nan("");
     a.stats[(bh * a.nQB + i0 + t) * 2 + 1] = __builtin_nan("");
   }
   fill_classes(a, NT, cls_s);
   if (select) {
     const ProxyTiles<D> pt(a, bh, i0, lane);
-    proxies_to_lds<D, NW>(a, pt, cr, wave, sv_s);
+    proxies_to_lds<D, NW, R>(a, pt, cr, wave, sv_s);
     __syncthreads();
-    for (int r = wave; r < 32; r += NW) {
+    for (int r = wave; r < R; r += NW) {
       if (i0 + r >= a.nQB) break;
       // the key of each register in three 32-bit words, most significant first;
       // bit k of live: candidate k of this lane still matches the prefix
@@ -859,7 +863,7 @@ __global__ __launch_bounds__(64 * NW) void decide_topk_lds_kernel(RouteArgs a) {
   }
   __syncthreads();
   // kept iff the key's first nb bits are >= the boundary prefix
-  write_map_rows(a, bh, i0, cr, NT, cls_s, [&](int r, int c) -> uint32_t {
+  write_map_rows<R>(a, bh, i0, cr, NT, cls_s, [&](int r, int c) -> uint32_t {
     if (!select) return keep > 0 ? 1u : (uint32_t)pruned;   // uniform
     const int nb = nb_s[r];
     const uint64_t hi = order_key(sv_s[r][c]), ph = phi_s[r];
@@ -947,11 +951,22 @@ static hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
     const dim3 grid((a.nQB + 31) / 32 * a.H * a.B);
     const CandRange cr(a);
     const bool lds = cr.jc1 - cr.jc0 <= kLdsCand;   // candidates' proxies fit in LDS
+    // 32-row workgroups take one CU each.  When there are more of them than
+    // CUs, the fixed-sparsity rule runs 16-row ones, two per CU: its per-row
+    // selection, which dominates, then spreads over twice the workgroups
+    // (measured 4 % faster route on the 32K workload).  The threshold rule
+    // stays at 32 rows: its per-row work is light, and 16-row workgroups would
+    // repeat the whole proxy pass (the 32-row tiles) for half the rows
+    // (measured 5 % slower).
+    const bool half = a.rule == kRuleTopK && (int64_t)grid.x > a.num_cus;
+    const dim3 grid16((a.nQB + 15) / 16 * a.H * a.B);
     if (a.rule == kRuleTopK) {
-      if (lds) decide_topk_lds_kernel<D, kLdsWaves><<<grid, 64 * kLdsWaves, 0, st>>>(a);
+      if (lds && half) decide_topk_lds_kernel<D, kLdsWaves, 16><<<grid16, 64 * kLdsWaves, 0, st>>>(a);
+      else if (lds) decide_topk_lds_kernel<D, kLdsWaves, 32><<<grid, 64 * kLdsWaves, 0, st>>>(a);
       else decide_topk_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);
     } else {
-      if (lds) decide_sol_lds_kernel<D, kLdsWaves><<<grid, 64 * kLdsWaves, 0, st>>>(a);
+      if (lds && half) decide_sol_lds_kernel<D, kLdsWaves, 16><<<grid16, 64 * kLdsWaves, 0, st>>>(a);
+      else if (lds) decide_sol_lds_kernel<D, kLdsWaves, 32><<<grid, 64 * kLdsWaves, 0, st>>>(a);
       else decide_sol_kernel<D><<<grid, 64 * kDecideWaves, 0, st>>>(a);
     }
   } else {

@@ -93,6 +93,7 @@ struct RouteArgs {
   double* stats;
   int8_t* qdig;    // workspace [B,H,nQB][2][d]: query-block column sums as two int8 digits (Sol rule only)
   int8_t* kdig;    // workspace [B,H,nKB][2][d]: key-block column sums, same form (Sol rule only)
+  int num_cus;     // compute units of the device (sizes the decision grid)
   const int16_t* q_sums;   // optional: the quantizer's column sums of Q per 128-row block [B,H,Lq/128,d]
   const int16_t* k_sums;   // optional: the same for K per 32-row chunk [B,H,Lkv/32,d]
 };

@@ -427,3 +427,17 @@ def test_batched(sa, orc, rule, G, prefix):
     wl.rule, wl.sparsity = rule, 0.5
     g, o = _check_workload(orc, wl)
     assert g["map"].shape[0] == B and not np.array_equal(g["map"][0], g["map"][1])
+
+
+@pytest.mark.parametrize("rule,G,d,L", [(0, 1, 64, 512), (1, 2, 128, 512), (1, 1, 64, 2560), (1, 0, 128, 512)])
+def test_decisions_in_sixteen_row_workgroups(sa, orc, rule, G, d, L):
+    """More 32-query-block decision chunks than compute units (260 heads):
+    the fixed-sparsity decisions run in 16-row workgroups, two per CU (the
+    threshold rule keeps 32-row ones).  L = 2560 gives 20 query blocks per
+    head: a full 16-row chunk and a ragged one."""
+    wl = W.tiny_sol(seed=111 + rule + d + G + L, H=260, L=L, d=d, valid=L - 42, centroids_per_block=max(G, 1))
+    wl.centroids_per_block = G
+    wl.rule, wl.sparsity = rule, 0.6
+    nQB = L // 128
+    g, o = _check_workload(orc, wl, tau=0.5, sel=np.arange(0, 260 * nQB, 7 * nQB // 4 + 1))
+    assert (g["map"] == (CENTROID if G > 0 else DROP)).any()
