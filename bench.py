@@ -15,6 +15,10 @@ every stage (their means give the roofline figures).  Then K more steps, each
 after an untimed 1 GiB write that evicts the 256 MB last-level cache, timed by
 events alone: medians with p10 and p90 per stage ("stages_cold_ms").
 
+After the timed steps a probe kernel measures this GPU's sustained
+matrix-core rate for the forward's op mix on random operands; the roofline
+object gives the forward's fraction of it beside the datasheet fractions.
+
 Prints one JSON line per workload.  value = dense-equivalent TOPS =
 4*B*H*Lq*Lkv*d / step time.  --peaks prints the measured matrix-core and HBM
 ceilings instead.
@@ -369,6 +373,10 @@ def run_case(n, args, sa, W, torch):
     peak_mixed = 1.0 / (0.5 / PEAK_INT8 + 0.5 / PEAK_BF16)
     if wl.qk_float:
         peak_mixed = PEAK_BF16   # both products on bf16 matrix cores
+    # the same GPU's sustained matrix-core rate for this op mix, measured now
+    mode = 1 if wl.qk_float else 2
+    measured_peak, _ = probe_mfma(torch, _probe_lib(), mode)
+    log(f"[bench] measured ceiling ({MFMA_PROBE_NAMES[mode]}): {measured_peak:.1f}")
     khash = kernel_hash()
     headline = n == 3 and not wl.qk_float and wl.rule == 0 and case.H == 40
     traffic = read_traffic(khash) if headline else None   # counters were taken on the headline workload
@@ -413,7 +421,12 @@ def run_case(n, args, sa, W, torch):
                                 else "sparse_attn_fwd (fwd_kernel<%d,false,%s,true>)" % (
                                     case.d, "true" if wl.v_int8 else "false")),
                      "ops_per_launch": ops, "fwd_ms_mean": round(fwd_ms, 4),
-                     "frac_of_int8_peak": round(achieved / PEAK_INT8, 4), "kernel_hash": khash},
+                     "frac_of_int8_peak": round(achieved / PEAK_INT8, 4),
+                     "measured_peak": round(measured_peak, 1),
+                     "frac_of_measured_peak": round(achieved / measured_peak, 4),
+                     "measured_peak_probe": ("bf16" if wl.qk_float else "50/50 int8/bf16") +
+                                            " MFMA loop on random operands, this GPU, after the timed steps",
+                     "kernel_hash": khash},
         "hbm_kernels": {},
     }
     for nm, nbytes in case.hbm_bytes().items():
@@ -520,16 +533,22 @@ def bench_cache_append(args, sa, W):
     print(json.dumps(res), flush=True)
 
 
-def bench_peaks(args):
-    """Matrix-core throughput (int8, bf16 and the forward's 50/50 mix, on
-    random operands) and HBM read / write / copy bandwidth, measured with the
-    probe kernels of libsa_probe.so."""
-    import torch
+def _probe_lib():
     lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_int8_amd", "libsa_probe.so"))
     lib.sa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_void_p]
     lib.sa_probe_bandwidth.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+MFMA_PROBE_NAMES = {0: "int8_mfma_TOPS", 1: "bf16_mfma_TFLOPS", 2: "mixed_50_50_TOPS"}
+
+
+def probe_mfma(torch, lib, mode, warmup=1, reps=3):
+    """Sustained matrix-core rate of this GPU on random operands, in TOP/s:
+    mode 0 int8 32x32x32, 1 bf16 32x32x16, 2 the forward's 50/50 mix (two int8
+    and four bf16 MFMAs per iteration, interleaved).  Median of `reps` runs."""
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     g = torch.Generator().manual_seed(7)
@@ -537,24 +556,37 @@ def bench_peaks(args):
     blocks = 256 * 8                       # 8 workgroups of 4 waves per CU: 8 waves per SIMD
     sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
     iters = 4096
-    res = {"metric": "MI355X measured ceilings (probe kernels)", "unit": "TOP/s | GB/s", "n_gpus": 1}
     # ops per MFMA: int8 32x32x32 = 2*32768, bf16 32x32x16 = 2*16384
-    per_wave = {0: iters * 4 * 65536, 1: iters * 4 * 32768, 2: iters * (2 * 65536 + 4 * 32768)}
-    names = {0: "int8_mfma_TOPS", 1: "bf16_mfma_TFLOPS", 2: "mixed_50_50_TOPS"}
+    per_wave = {0: iters * 4 * 65536, 1: iters * 4 * 32768, 2: iters * (2 * 65536 + 4 * 32768)}[mode]
+    ts = []
+    for rep in range(reps + warmup):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert lib.sa_probe_mfma(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(sink.data_ptr()), mode, iters,
+                                 blocks, sp) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rep >= warmup:
+            ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    return per_wave * blocks * 4 / (ms * 1e-3) / 1e12, ms
+
+
+def bench_peaks(args):
+    """Matrix-core throughput (int8, bf16 and the forward's 50/50 mix, on
+    random operands) and HBM read / write / copy bandwidth, measured with the
+    probe kernels of libsa_probe.so."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.zeros(256 * 8 * 256, dtype=torch.int32, device="cuda")
+    res = {"metric": "MI355X measured ceilings (probe kernels)", "unit": "TOP/s | GB/s", "n_gpus": 1}
     for mode in (0, 1, 2):
-        best = []
-        for rep in range(3 + args.warmup):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            assert lib.sa_probe_mfma(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(sink.data_ptr()), mode, iters,
-                                     blocks, sp) == 0
-            e1.record(stream)
-            torch.cuda.synchronize()
-            if rep >= args.warmup:
-                best.append(e0.elapsed_time(e1))
-        ms = float(np.median(best))
-        res[names[mode]] = round(per_wave[mode] * blocks * 4 / (ms * 1e-3) / 1e12, 1)
-        log(f"[peaks] {names[mode]}: {res[names[mode]]} ({ms:.3f} ms)")
+        tops, ms = probe_mfma(torch, lib, mode, warmup=args.warmup)
+        nm = MFMA_PROBE_NAMES[mode]
+        res[nm] = round(tops, 1)
+        log(f"[peaks] {nm}: {res[nm]} ({ms:.3f} ms)")
     nbytes = 2 << 30
     x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
     y = torch.empty(nbytes, dtype=torch.uint8, device="cuda")

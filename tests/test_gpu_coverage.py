@@ -319,3 +319,50 @@ def test_route_reads_no_codes_when_given_sums(sa):
     torch.cuda.synchronize()
     for got, key in ((bmap, "map"), (kc, "k_centroid"), (vc, "v_centroid"), (cnt, "count"), (st, "row_stats")):
         assert torch.equal(got, ref[key]), key
+
+
+# ---------------------------------------------------------------------------
+# Neighbouring query blocks with different maps (d = 128, bf16 V)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,L,valid", [(1, 1152, 1100), (2, 1024, 1000), (0, 640, 577)])
+def test_neighbouring_blocks_with_differing_maps(sa, orc, G, L, valid):
+    """Neighbouring query blocks keep different tiles (random explicit maps),
+    with an odd number of query blocks and tiles that hold the end of the
+    valid keys."""
+    H = 3
+    wl = W.tiny_sol(seed=140 + G + L, H=H, L=L, d=128, valid=valid, centroids_per_block=max(G, 1))
+    wl.centroids_per_block = G
+    rng = np.random.default_rng(141 + G)
+    states = np.array([EXACT, CENTROID, DROP] if G > 0 else [EXACT, DROP], np.uint8)
+    probs = [0.5, 0.35, 0.15] if G > 0 else [0.6, 0.4]
+    wl.explicit_map = rng.choice(states, size=(1, H, L // 128, L // 64), p=probs)
+    g, o = _check_workload(orc, wl)
+    gm = g["map"]
+    assert (gm[:, :, 0::2][:, :, :gm.shape[2] // 2] != gm[:, :, 1::2]).any()
+
+
+def test_dropped_tile_does_not_reach_a_block(sa, orc):
+    """A tile that one query block keeps and its neighbour drops reaches only
+    the block that keeps it: a NaN or Inf in its V rows leaves the other
+    block's outputs as they are without the tile."""
+    H, L = 1, 512
+    wl = W.tiny_sol(seed=150, H=H, L=L, d=128, valid=L, centroids_per_block=1)
+    wl.centroids_per_block = 0
+    em = np.full((1, H, L // 128, L // 64), EXACT, np.uint8)
+    em[0, 0, 0::2, 3] = DROP       # blocks 0 and 2 drop key blocks 3 and 5, blocks 1 and 3 keep them
+    em[0, 0, 0::2, 5] = DROP
+    wl.explicit_map = em
+    v = wl.v.copy()
+    v[0, 0, 3 * 64 + 7, 11] = 0x7FC0     # bf16 NaN in a valid row of key block 3
+    v[0, 0, 5 * 64 + 60, 0] = 0x7F80     # bf16 +Inf in key block 5
+    wl.v = v
+    say("case non-finite V in tiles that every other query block drops")
+    g = gpu_pipeline(wl)
+    o = orc.run(wl)
+    out = g["out"].reshape(4, 128, 128)
+    assert np.isfinite(out[0]).all() and np.isfinite(out[2]).all()
+    assert not np.isfinite(out[1]).all() and not np.isfinite(out[3]).all()
+    for b in (0, 2):
+        err = np.abs(out[b] - o["out"][b])
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
