@@ -300,10 +300,20 @@ struct ProxyTiles {
     const int nj = j < a.nKB ? a.lay.block_rows(j) : 0;
     const double bj = nj > 0 ? (double)a.k_scale[bh * nKS + j] : 0.0, nd = nj > 0 ? (double)nj : 1.0;
     // D is an exact integer in float64; then one rounding for the product
-    // and one for the quotient, in that order
+    // and one for the quotient, in that order.  A full block has a power of
+    // two rows, and dividing by a power of two only shifts the exponent, so
+    // there round(D*b)/n = D*(b/n) exactly: one multiply.  Other blocks (the
+    // last one of a segment) divide.
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      sv[e] = ((16384.0 * (double)p1[e] + 128.0 * (double)p2[e] + (double)p3[e]) * bj) / nd;
+    for (int e = 0; e < 16; ++e) sv[e] = 16384.0 * (double)p1[e] + 128.0 * (double)p2[e] + (double)p3[e];
+    if ((nj & (nj - 1)) == 0) {
+      const double cj = bj / nd;   // exact
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sv[e] *= cj;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sv[e] = (sv[e] * bj) / nd;
+    }
   }
   __device__ __forceinline__ int row_of(int e) const { return (e / 4) * 8 + hf * 4 + (e % 4); }
 };
