@@ -128,6 +128,9 @@ def _route(dims, prm, em=None, ws=None, wsb=0, G_out=True):
     ({}, dict(segments=[(0, 64, 0), (192, 100, 1)]), sa.SA_E_VALUE, "rows 100 outside"),
     ({}, dict(segments=[(0, 64, 0)], prefix_tokens=64), sa.SA_E_VALUE, "prefix_tokens must be 0"),
     ({}, dict(segments=[(64 * x, 1, 0) for x in range(17)]), sa.SA_E_VALUE, "n_segments"),
+    (dict(Lkv=6146 * 64, lkv_valid=6146 * 64, Lv=6146 * 64), {}, sa.SA_E_SHAPE, "at most 6144 key blocks"),
+    (dict(Lkv=6146 * 64, lkv_valid=6146 * 64, Lv=6146 * 64), dict(rule=sa.SA_RULE_TOPK, sparsity=0.5),
+     sa.SA_E_SHAPE, "at most 6144 key blocks"),
 ])
 def test_route_validation(dims_kw, prm_kw, code, msg):
     assert _route(_dims(**dims_kw), _prm(**prm_kw)) == code

@@ -381,6 +381,27 @@ def test_float_qk_and_topk_degenerate(sa, orc):
     assert ((g["map"][..., :5] == 1).sum(-1) == 1).all()
 
 
+@pytest.mark.parametrize("rule,G", [(0, 1), (1, 0)])
+def test_max_key_blocks(sa, orc, rule, G):
+    """The longest rows the routing rules accept: 6144 key blocks of 64 rows
+    (393216 keys; the forward walks its block map in 12 windows of 512), with
+    a ragged end of the keys and of the queries."""
+    rng = np.random.default_rng(171 + 64 + rule)
+    H, Lq, Lkv, d = 2, 128, 6144 * 64, 64
+    lq_valid, lkv_valid = Lq - 3, Lkv - 21
+    q = W.iid_normal_bf16(rng, (1, H, Lq, d))
+    k = W.iid_normal_bf16(rng, (1, H, Lkv, d))
+    v = W.iid_normal_bf16(rng, (1, H, Lkv, d))
+    for t in (k, v):
+        t[0, :, lkv_valid:] = 0            # padding rows hold zeros
+    q[0, :, lq_valid:] = 0
+    wl = W.Workload("max_key_blocks", 1, H, Lq, Lkv, d, lq_valid, lkv_valid, q, k, v, threshold=1.0,
+                    centroids_per_block=G, kblock=64, k_scale_rows=64)
+    wl.rule, wl.sparsity = rule, 0.6
+    g, o = _check_workload(orc, wl)
+    assert (g["map"] == EXACT).sum() > 4000 and (g["map"] != EXACT).sum() > 1000
+
+
 @pytest.mark.parametrize("rule,d,G,prefix", [(0, 128, 1, 0), (1, 128, 1, 1024), (0, 64, 2, 1024), (1, 64, 0, 0)])
 def test_long_rows(sa, orc, rule, d, G, prefix):
     """Rows with more than 512 candidate key blocks (here up to 640) take the
