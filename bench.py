@@ -249,16 +249,17 @@ class Case:
         return out
 
     def plain_route_bytes(self):
-        """The route's bytes by the survey's measurement plan: int8 Q, int8 K and
-        V read, centroids, counts and the map written."""
+        """The route's bytes when it reads the int8 codes themselves: int8 Q,
+        int8 K and V read, centroids, counts and the map written (the count the
+        measurement plan of this path fixes for the route)."""
         wl, B, H, d = self.wl, self.B, self.H, self.d
         nQB, nKB = self.Lq // 128, self.Lkv // self.kb
         qe, ke = B * H * self.Lq * d, B * H * self.Lkv * d
         return qe + ke + B * H * wl.v.shape[2] * d * 2 + B * H * nKB * self.G * (2 * d + 1) * 4 + B * H * nQB * nKB
 
     def plain_bytes(self):
-        """The bytes the survey's measurement plan assigns to quantizing Q and
-        K and to the route (int8 Q, int8 K and V read by the route, outputs
+        """The bytes the measurement plan of this path assigns to quantizing Q
+        and K and to the route (int8 Q, int8 K and V read by the route, outputs
         written), for the routed workloads: their sum over the three stages'
         time is the like-for-like HBM figure whichever stage reads what."""
         wl, B, H, d = self.wl, self.B, self.H, self.d
@@ -443,13 +444,13 @@ def run_case(n, args, sa, W, torch):
         res["hbm_kernels"][nm] = {"bytes": int(nbytes), "GB/s": round(gbs, 1),
                                   "frac_of_8TB/s": round(gbs / PEAK_HBM, 4)}
     if wl.explicit_map is None and not wl.virtual:
-        # the route by the survey's byte count (it reads the quantizer's column
-        # sums instead of the codes, so it moves fewer bytes than that count)
+        # the route by the byte count of a route that reads the codes (this one
+        # reads the quantizer's column sums instead, so it moves fewer bytes)
         rb = case.plain_route_bytes()
         i = case.stage_names.index("route")
         gbs = rb / (stage_mean[i] * 1e-3) / 1e9
-        res["hbm_kernels"]["route"].update({"bytes_survey_plan": int(rb), "GB/s_survey_plan": round(gbs, 1),
-                                            "frac_of_8TB/s_survey_plan": round(gbs / PEAK_HBM, 4)})
+        res["hbm_kernels"]["route"].update({"bytes_if_reading_codes": int(rb), "GB/s_if_reading_codes": round(gbs, 1),
+                                            "frac_of_8TB/s_if_reading_codes": round(gbs / PEAK_HBM, 4)})
         nbytes = case.plain_bytes()
         ms3 = float(stage_mean[0] + stage_mean[1] + stage_mean[2])
         gbs = nbytes / (ms3 * 1e-3) / 1e9
