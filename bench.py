@@ -127,6 +127,8 @@ class Case:
         t = time.perf_counter()
         if n == 3:
             wl = W.wan_like(H=args.heads)
+        elif n == SEG:
+            wl = W.ref2va_segments()
         else:
             wl = W.config(n)
         if args.rule == "topk" and wl.explicit_map is None:
@@ -200,7 +202,8 @@ class Case:
                                       prefix_tokens=wl.prefix_tokens, kblock=self.kb, k_scale_rows=wl.k_scale_rows,
                                       v_scale_rows=wl.v_scale_rows, explicit_map=self.em, map_kblock=wl.map_kblock,
                                       rule=wl.rule, sparsity=wl.sparsity, workspace=self.ws, outputs=self.routed,
-                                      q_sums=self.qsum if wl.explicit_map is None else None, k_sums=self.ksum)
+                                      q_sums=self.qsum if wl.explicit_map is None else None, k_sums=self.ksum,
+                                      segments=wl.segments)
         self.ws = r["workspace"]
 
     def fwd(self, out_dtype=None, out=None):
@@ -208,7 +211,7 @@ class Case:
         kw = dict(k_centroid=r.get("k_centroid"), v_centroid=r.get("v_centroid"), count=r.get("count"),
                   lq_valid=wl.lq_valid, lkv_valid=wl.lkv_valid, centroids_per_block=self.G, kblock=self.kb,
                   sm_scale=wl.sm_scale, out_dtype=out_dtype or self.torch.bfloat16,
-                  out=self.out if out is None else out)
+                  out=self.out if out is None else out, segments=wl.segments)
         if wl.qk_float:
             self.sa.sparse_attn_fwd_float(self.q, self.k, self.v, r["map"], v_block_src=self.vbs, **kw)
         else:
@@ -277,7 +280,9 @@ class Case:
                     f"{rule}",
                  3: f"Wan-14B-like Sol 1x64: B=1 H={self.H} d=128 L=32768 (32760 valid), {rule}",
                  4: f"Sol 2x32 with 1024-token dense prefix: B=1 H={self.H} d=128 L={self.Lq}, {rule}",
-                 5: f"virtual KV residual: B=1 H={self.H} d=128 Lq={self.Lq} Lkv={self.Lkv} logical, {rule}"}
+                 5: f"virtual KV residual: B=1 H={self.H} d=128 Lq={self.Lq} Lkv={self.Lkv} logical, {rule}",
+                 SEG: f"segmented Ref2VA-like layout: B=1 H={self.H} d=128 L={self.Lq} (text, reference image and "
+                      f"audio dense; reference video and 8 generated frames routed), {rule}"}
         return names[self.n]
 
 
@@ -319,7 +324,9 @@ def cpu_baseline(case, stride: int):
                 threads=oracle.num_threads(), sel=sel, out=out, map=r["map"], tie=r["tie"])
 
 
-CPU_STRIDE = {1: 1, 2: 1, 3: 40, 4: 24, 5: 1}
+# workload id of the segmented key layout (--config seg)
+SEG = 6
+CPU_STRIDE = {1: 1, 2: 1, 3: 40, 4: 24, 5: 1, SEG: 12}
 
 
 def run_case(n, args, sa, W, torch):
@@ -397,6 +404,8 @@ def run_case(n, args, sa, W, torch):
         metric = METRIC if wl.rule == 0 else METRIC.replace("thr=1.0", f"top-k sparsity={wl.sparsity:g}")
         if wl.qk_float:
             metric += ", bf16 QK"
+    elif n == SEG:
+        metric = "sparse attn fwd ms + dense-equiv TOPS, segmented key layout (Ref2VA-like, H=24, d=128)"
     else:
         metric = f"sparse attn fwd ms + dense-equiv TOPS, workload {n} ({W.CONFIG_NAMES[n]})"
     res = {
@@ -411,7 +420,9 @@ def run_case(n, args, sa, W, torch):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 QK^T + fp32 softmax + bf16 PV" if wl.qk_float else "int8 QK^T + fp32 softmax + bf16 PV",
-        "data": "synthetic (seeded bf16 Q/K/V; " + ("per-frame low-rank correlated)" if n in (3, 4) else "N(0,1))"),
+        "data": "synthetic (seeded bf16 Q/K/V; " + ("per-frame low-rank correlated)" if n in (3, 4) else
+                                                    "N(0,1) conditioning segments, per-frame low-rank correlated video)"
+                                                    if n == SEG else "N(0,1))"),
         "config": {"workload": case.workload_desc(), "B": case.B, "H": case.H, "Lq": case.Lq, "Lkv": case.Lkv,
                    "d": case.d, "lq_valid": wl.lq_valid, "lkv_valid": wl.lkv_valid, "kblock": case.kb,
                    "centroids": {0: "none", 1: "1x64", 2: "2x32"}[case.G],
@@ -658,7 +669,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="3",
-                    help="workload 1..5 (3 is the measured one; the others are the parity workloads), or 'all'")
+                    help="workload 1..5 (3 is the measured one; the others are the parity workloads), 'all' (1..5), "
+                         "or 'seg' (the segmented key layout of the reference-conditioned video recipe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-stride", type=int, default=0,
                     help="oracle forward on every n-th query block (0: a per-workload default)")
@@ -693,7 +705,8 @@ def main():
     if args.cache_append:
         bench_cache_append(args, sa, W)
         return
-    configs = [1, 2, 3, 4, 5] if args.config == "all" else [int(args.config)]
+    configs = ([1, 2, 3, 4, 5] if args.config == "all" else [SEG] if args.config == "seg"
+               else [int(args.config)])
     for n in configs:
         run_case(n, args, sa, W, torch)
 
