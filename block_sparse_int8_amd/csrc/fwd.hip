@@ -233,8 +233,10 @@ struct TileInfo {
   int nvb;                // V blocks of the tensor (clamp bound), 0 when V rows are not remapped
   float kscale, pscale;
   __device__ __forceinline__ int vrow0() const {
-    const int vb = nvb > 0 ? min(max(vblk, 0), nvb - 1) : vblk;
-    return __builtin_amdgcn_readfirstlane(vb) * kTile;
+    // the entry is wave-uniform: clamp it on the scalar unit
+    const int v = __builtin_amdgcn_readfirstlane(vblk);
+    const int vb = nvb > 0 ? min(max(v, 0), nvb - 1) : v;
+    return vb * kTile;
   }
 };
 
@@ -768,8 +770,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       // spreading them over both steps or issuing two per segment).
       constexpr int PH = TileCopy<D, KB, VI8>::PIECES;   // copy pieces in a tile's first step
       constexpr int PN = TileCopy<D, KB, VI8>::PIECES;
-      TileInfo t0 = fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[0]), nKS, nVS);
-      TileInfo t1 = nE > 1 ? fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + elist[1]), nKS, nVS) : t0;
+      TileInfo t0 = fetch_tile<QF, VI8>(a, bh, w0 * tpb + __builtin_amdgcn_readfirstlane(elist[0]), nKS, nVS);
+      TileInfo t1 = nE > 1 ? fetch_tile<QF, VI8>(a, bh, w0 * tpb + __builtin_amdgcn_readfirstlane(elist[1]), nKS, nVS) : t0;
       // list entry of tile T + 2, read one iteration before it is needed so
       // the top of an iteration does not wait for an LDS read
       int next_entry = elist[min(2, nE - 1)];
@@ -797,7 +799,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         uint8_t* const vwr = ODD ? vst0 : vst1;   // V of tile T+1 goes here
         copies_done_barrier();
         const TileInfo t2 =
-            T + 2 < nE ? fetch_tile<QF, VI8>(a, bh, __builtin_amdgcn_readfirstlane(w0 * tpb + next_entry), nKS, nVS)
+            T + 2 < nE ? fetch_tile<QF, VI8>(a, bh, w0 * tpb + __builtin_amdgcn_readfirstlane(next_entry), nKS, nVS)
                        : t1;
         next_entry = elist[min(T + 3, nE - 1)];
         if (VI8) load_v_int8<D>(v8base + (int64_t)t1.vrow0() * D, vr, tid);
