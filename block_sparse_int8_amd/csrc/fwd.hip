@@ -861,7 +861,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const float* cnh = a.cnt + chead;
     for (int c0 = 0; c0 < ncols; c0 += 32) {
       {
-        const int col = tid >> 3, q = tid & 7;
+        // INT8 V: thread roles formed again from the thread index here; hoisted
+        // out of the window loop, the per-thread addresses would live across
+        // the tile loop next to the V staging registers (and be spilled)
+        const int st = VI8 ? opaque(tid) : tid, col = st >> 3, q = st & 7;
         const int ent = c0 + col, be = a.G == 2 ? ent >> 1 : ent, g = a.G == 2 ? ent & 1 : 0;
         float cn = 0.0f;
         float4 kv[CE], vv[CE];
@@ -909,7 +912,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           qb = qf.q[s];
           ch = s * 16 + hh * 8;
         } else {
-          qb = i8x8_to_bf16(qf.q[s / 2][2 * (s % 2)], qf.q[s / 2][2 * (s % 2) + 1]);
+          v4i qv = qf.q[s / 2];
+          // INT8 V: converted here each batch; hoisted out of the loops, the
+          // bf16 query would stay live across the tile loop and be spilled
+          if (VI8) asm volatile("" : "+v"(qv));
+          qb = i8x8_to_bf16(qv[2 * (s % 2)], qv[2 * (s % 2) + 1]);
           ch = (s / 2) * 32 + hh * 16 + (s % 2) * 8;
         }
         const int off = L::kc_off(n, ch * 2);
