@@ -74,3 +74,30 @@ def test_pipeline_graph_replay(sa, rule):
     g.replay()
     torch.cuda.synchronize()
     assert _same(captured, ref2), "replay on new inputs differs from their eager run"
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_pipeline_on_a_side_stream(sa, rule):
+    """The whole path queued on a stream other than torch's current one: the
+    binding records that stream on every tensor it allocates, so memory the
+    caching allocator hands out on the current stream right after the call
+    returns (before the side stream has run) is not memory the kernels still
+    use.  The result must equal the current-stream run bit for bit."""
+    say(f"case side stream rule={rule}")
+    kw = dict(lq_valid=1000, lkv_valid=1000, threshold=1.0, centroids_per_block=1, rule=rule, sparsity=0.6,
+              out_dtype=torch.float32, return_lse=True)
+    q, k, v = _inputs(73)
+    (ref_out, ref_lse), ref_map = sa.sparse_attention(q, k, v, **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    hold = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    torch.cuda._sleep(50_000_000)                 # keep the side stream's work queued behind the sleep
+    side.wait_stream(torch.cuda.current_stream())
+    (out, lse), bmap = sa.sparse_attention(q, k, v, stream=side, **kw)
+    # while the side stream waits: allocate and fill on the current stream
+    junk = [torch.full((1 << 20,), float(i), device="cuda") for i in range(16)]
+    del junk, hold
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse) and torch.equal(bmap, ref_map)
