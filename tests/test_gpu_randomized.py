@@ -1,11 +1,13 @@
 """Seeded randomized GPU parity: combinations of head size, key-block size,
 centroid groups, routing rule, segmented key layouts with padding, valid
-lengths and the floating QK path, each checked against the oracle to the
-same bars as the hand-picked cases."""
+lengths and the floating QK path, and of the INT8 K/V cache path (rules or
+explicit maps), each checked against the oracle to the same bars as the
+hand-picked cases."""
 import numpy as np
 import pytest
 
 import workloads as W
+from workloads import CENTROID, DROP, EXACT
 from tests.test_gpu_parity import _check_workload, sa  # noqa: F401  (fixture)
 
 pytestmark = pytest.mark.gpu
@@ -64,3 +66,43 @@ def test_random_configuration_medium(sa, orc, seed):
     of workgroups, longer tile lists and their ragged ends."""
     wl = random_case(seed, max_blocks=12)
     _check_workload(orc, wl, sums=seed % 2 == 1)
+
+
+def random_int8v_case(seed: int) -> W.Workload:
+    """K and V as an INT8 cache (FlashVSR Kitchen Sparse Attention, opening
+    section): random head size, key-block size, V scale rows, ragged valid
+    lengths, and either a routing rule or an explicit EXACT / CENTROID / DROP
+    map (where K may carry one scale per 64 rows under 128-key blocks)."""
+    rng = np.random.default_rng(5000 + seed)
+    d = int(rng.choice([64, 128]))
+    kblock = int(rng.choice([64, 128]))
+    H = int(rng.integers(1, 4))
+    L = 128 * int(rng.integers(2, 17))
+    lkv_valid = int(rng.integers(L // 2, L + 1))
+    lq_valid = int(rng.choice([L, int(rng.integers(1, L + 1))]))
+    mode = int(rng.integers(0, 3))            # 0 threshold, 1 fixed sparsity, 2 explicit map
+    G = int(rng.integers(1, 3)) if mode == 0 else int(rng.integers(0, 3))
+    q = W.iid_normal_bf16(rng, (1, H, L, d))
+    k = W.iid_normal_bf16(rng, (1, H, L, d))
+    v = W.iid_normal_bf16(rng, (1, H, L, d))
+    for t in (k, v):
+        t[0, :, lkv_valid:] = 0
+    q[0, :, lq_valid:] = 0
+    ksr = kblock if mode < 2 else int(rng.choice([64, kblock]))
+    wl = W.Workload(f"random_int8v_{seed}", 1, H, L, L, d, lq_valid, lkv_valid, q, k, v,
+                    threshold=float(rng.uniform(-0.5, 1.5)), centroids_per_block=G, kblock=kblock,
+                    k_scale_rows=ksr, v_int8=True, v_scale_rows=int(rng.choice([64, 128])))
+    if mode == 1:
+        wl.rule, wl.sparsity = 1, float(rng.choice([0.0, 0.5, 0.75, 1.0]))
+    elif mode == 2:
+        states = np.array([EXACT, CENTROID, DROP] if G > 0 else [EXACT, DROP], np.uint8)
+        wl.explicit_map = rng.choice(states, size=(1, H, L // 128, L // kblock))
+        wl.map_kblock = kblock
+        wl.threshold = float("nan")
+    return wl
+
+
+@pytest.mark.parametrize("seed", range(96))
+def test_random_int8_cache_configuration(sa, orc, seed):
+    wl = random_int8v_case(seed)
+    _check_workload(orc, wl, sums=seed % 2 == 0)
