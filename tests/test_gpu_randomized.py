@@ -1,7 +1,7 @@
 """Seeded randomized GPU parity: combinations of head size, key-block size,
 centroid groups, routing rule, segmented key layouts with padding, valid
-lengths and the floating QK path, and of the INT8 K/V cache path (rules or
-explicit maps), each checked against the oracle to the same bars as the
+lengths and the floating QK path, of the INT8 K/V cache path (rules or
+explicit maps) and of virtual K/V, each checked against the oracle to the same bars as the
 hand-picked cases."""
 import numpy as np
 import pytest
@@ -105,4 +105,46 @@ def random_int8v_case(seed: int) -> W.Workload:
 @pytest.mark.parametrize("seed", range(96))
 def test_random_int8_cache_configuration(sa, orc, seed):
     wl = random_int8v_case(seed)
+    _check_workload(orc, wl, sums=seed % 2 == 0)
+
+
+def random_virtual_case(seed: int) -> W.Workload:
+    """Virtual K/V (Configure H3 Static Virtual KV, mode list): logical slices
+    gathered from random physical ones with temporal RoPE on a random even
+    channel span; then an explicit map, the Sol rule or fixed sparsity over
+    the logical keys, with bf16 or INT8 V read through the V block table."""
+    rng = np.random.default_rng(7000 + seed)
+    d = int(rng.choice([64, 128]))
+    H = int(rng.integers(1, 4))
+    S = 128 * int(rng.integers(1, 5))                 # rows per slice
+    n_phys = int(rng.integers(1, 4))
+    n_logical = int(rng.integers(max(n_phys, 2), 8))
+    src = rng.integers(0, n_phys, n_logical).astype(np.int32)
+    rot_offset = 2 * int(rng.integers(0, d // 4))
+    d_rot = 2 * int(rng.integers(1, (d - rot_offset) // 2 + 1))
+    cos, sin = W.rope_tables(n_logical, d_rot)
+    Lq = 128 * int(rng.integers(1, n_phys * S // 128 + 1))
+    Lkv = n_logical * S
+    q = W.iid_normal_bf16(rng, (1, H, Lq, d))
+    k = W.iid_normal_bf16(rng, (1, H, n_phys * S, d))
+    v = W.iid_normal_bf16(rng, (1, H, n_phys * S, d))
+    mode = int(rng.integers(0, 3))                    # 0 explicit map, 1 threshold, 2 fixed sparsity
+    G = int(rng.integers(0 if mode != 1 else 1, 3))
+    wl = W.Workload(f"random_virtual_{seed}", 1, H, Lq, Lkv, d, Lq, Lkv, q, k, v,
+                    threshold=float(rng.uniform(-0.5, 1.5)), centroids_per_block=G, kblock=64, k_scale_rows=64,
+                    virtual=True, rows_per_slice=S, n_phys=n_phys, src_map=src, rope_cos=cos, rope_sin=sin,
+                    rot_offset=rot_offset, d_rot=d_rot)
+    wl.v_int8, wl.v_scale_rows = bool(rng.integers(0, 2)), 128
+    if mode == 0:
+        states = np.array([EXACT, CENTROID, DROP] if G > 0 else [EXACT, DROP], np.uint8)
+        wl.explicit_map = rng.choice(states, size=(1, H, Lq // 128, Lkv // 64))
+        wl.threshold = float("nan")
+    elif mode == 2:
+        wl.rule, wl.sparsity = 1, float(rng.choice([0.0, 0.5, 0.75, 1.0]))
+    return wl
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_virtual_configuration(sa, orc, seed):
+    wl = random_virtual_case(seed)
     _check_workload(orc, wl, sums=seed % 2 == 0)
